@@ -1,0 +1,193 @@
+"""Benchmark of the KDA recurrent prefill forward on one MI355X.
+
+One step = one kda_fwd launch over the whole workload (every chunk of every
+(sequence, head)), inputs already resident in device memory.  Prints one JSON
+line.  The default workload is B=2, T=1024, H=96, D=128 with a bf16 initial
+state ~ N(0, 0.1^2) and a bf16 final state.
+
+Roofline accounting (per launch):
+  algorithmic bytes = token-heads * (8 D + 2 + 2 D)   (q, k, v, g, beta in; out)
+                    + states in and out + A_log + dt_bias
+  counted FLOP      = token-heads * 7 * D * D          (the per-token recurrence:
+                      decay D^2, S k 2 D^2, rank-1 update 2 D^2, S q 2 D^2)
+The kernel is HBM-bound at this arithmetic intensity (about 85 FLOP/B against a
+ridge of about 315), so the roofline object reports bytes against 8 TB/s; the
+fraction of the bf16 MFMA peak (2.5 PFLOP/s dense) is reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6
+METRIC = "prefill tokens/sec (H=96,D=128) + % of MI355X bf16 MFMA peak"
+PMC_PROFILE = os.path.join(ROOT, "profiles", "kda_fwd_batched_pmc.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_62_amd", "csrc", f)
+                  for f in ("kda_kernel.hip", "kda_params.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(inp) -> int:
+    B, T, H, D = inp["q"].shape
+    th = B * T * H
+    b = th * (8 * D + 2 + 2 * D)
+    for s in (inp["initial_state"], inp["final_state"]):
+        if s is not None:
+            b += s.numel() * s.element_size()
+    b += inp["A_log"].numel() * 4 + inp["dt_bias"].numel() * 4
+    return int(b)
+
+
+def counted_flops(inp) -> int:
+    B, T, H, D = inp["q"].shape
+    return int(B * T * H * 7 * D * D)
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    if not os.path.exists(PMC_PROFILE):
+        return None
+    text = open(PMC_PROFILE).read()
+    m_hash = re.search(r"kernel_source_hash:\s*(\w+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(inp, heads: int):
+    """Times the fp64 oracle on a sample of heads of the same workload (host cores)."""
+    import oracle
+    import torch
+    B, T, H, D = inp["q"].shape
+    hs = list(range(0, H, max(1, H // heads)))[:heads]
+    sel = lambda t: t[:, :, hs].to("cpu")
+    args = [sel(inp[n]) for n in ("q", "k", "v", "g", "beta")]
+    s0 = inp["initial_state"]
+    s0 = None if s0 is None else s0[:, hs].to("cpu")
+    A_log, dt_bias = inp["A_log"][hs].cpu(), inp["dt_bias"][hs].cpu()
+    cu = inp["cu_seqlens"].cpu() if inp["cu_seqlens"] is not None else None
+    oracle._load()
+    # widen to fp64 outside the timed region, exactly as the oracle would
+    import numpy as np
+    wide = [np.ascontiguousarray(a.to(torch.float64).numpy()) for a in args]
+    s0w = None if s0 is None else np.ascontiguousarray(s0.to(torch.float64).numpy())
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    oracle.kda_fwd(*wide, inp["scale"], A_log.double().numpy(), dt_bias.double().numpy(),
+                   inp["lower_bound"], s0w, cu, nthreads=threads)
+    wall = time.perf_counter() - t0
+    sample_token_heads = B * T * len(hs)
+    return {"value": sample_token_heads / wall / H, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "fp64 per-token recurrence on %d of %d heads (all %d tokens of each), "
+                      "%.2f s wall; tokens/s scaled to all %d heads" % (len(hs), H, B * T, wall,
+                                                                        H)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="batched")
+    ap.add_argument("--chunk", type=int, default=None, help="force the chunk size")
+    ap.add_argument("--v-tile", type=int, default=0, help="force the value tile")
+    ap.add_argument("--cpu-heads", type=int, default=24,
+                    help="heads of the workload the CPU oracle baseline runs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the KDA prefill kernel runs on a single "
+              "MI355X here and this build has no multi-GPU path (heads or sequences would be "
+              "sharded across GPUs with no exchange). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_62_amd as kda
+    from gated_delta_rule_62_amd.workloads import WORKLOADS, make_inputs, token_heads
+
+    w = WORKLOADS[args.workload]
+    chunk = w.chunk_size if args.chunk is None else args.chunk
+    inp = make_inputs(w, device="cuda")
+    B, T, H, D = inp["q"].shape
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.kda_fwd_sched(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"],
+                          inp["out"], inp["A_log"], inp["dt_bias"], inp["lower_bound"],
+                          inp["initial_state"], inp["final_state"], inp["cu_seqlens"],
+                          chunk_size=chunk, v_tile=args.v_tile, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_launch = ev0.elapsed_time(ev1) / args.steps
+    tokens = B * T
+    value = tokens * args.steps / wall
+
+    nbytes = algorithmic_bytes(inp)
+    flops = counted_flops(inp)
+    achieved = nbytes / (ms_per_launch * 1e-3) / 1e9
+    tflops = flops / (ms_per_launch * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "kda_fwd %s: B=%d T=%d H=%d D=%d, bf16 q/k/v/g/beta ~N(0,1), "
+                               "lower_bound=%g, state %s->%s" % (
+                                   w.name, B, T, H, D, w.lower_bound, w.state_in, w.state_out),
+                   "B": B, "T": T, "H": H, "D": D, "token_heads": token_heads(inp),
+                   "chunk": chunk or "auto", "v_tile": args.v_tile or "auto"},
+        "mfma_pct_of_bf16_peak": 100.0 * tflops / MFMA_BF16_PEAK_TFLOPS,
+        "kernel_ms": ms_per_launch,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "algorithmic_bytes": nbytes, "counted_tflops": tflops},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_heads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

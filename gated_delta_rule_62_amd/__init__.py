@@ -1,0 +1,158 @@
+"""MI355X (gfx950) KDA recurrent prefill forward.
+
+A thin ctypes binding over ``libkda.so`` (built from ``csrc/`` with hipcc): it
+checks tensor dtypes, devices and contiguity, passes raw device pointers, sizes
+and torch's current HIP stream to the C ABI declared in ``include/kda.h``, and
+turns status codes into exceptions.  Every step of the computation runs in the
+library's kernels; there is no other code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from ._build import LIB_PATH, build  # noqa: F401  (build() is the in-tree compile step)
+
+__all__ = ["kda_fwd", "kda_fwd_sched", "kda_fwd_check", "kda_chunk_anchor",
+           "kda_status_string", "KdaError", "library_path", "load_library"]
+
+KDA_OK = 0
+KDA_ERR_NULL_ARG = -1
+KDA_ERR_BAD_SHAPE = -2
+KDA_ERR_BAD_DTYPE = -3
+KDA_ERR_BAD_VARLEN = -4
+KDA_ERR_BAD_ALIAS = -5
+KDA_ERR_BAD_LOWER_BOUND = -6
+KDA_ERR_BAD_SCALE = -7
+KDA_ERR_BAD_SCHEDULE = -8
+KDA_ERR_HIP = -9
+KDA_DTYPE_BF16 = 0
+KDA_DTYPE_FP32 = 1
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(kda_status_string(status))
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library():
+    """Load ``libkda.so``; raises if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libkda.so is not built at %s; run gated_delta_rule_62_amd.build() "
+                          "(or __graft_entry__.build())" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    common = [vp, vp, vp, vp, vp, f32, vp, vp, vp, f32, vp, i32, vp, i32, vp, i64, i64, i64, i64,
+              i64]
+    lib.kda_fwd.argtypes = common + [vp]
+    lib.kda_fwd.restype = i32
+    lib.kda_fwd_sched.argtypes = common + [vp, i32, i32]
+    lib.kda_fwd_sched.restype = i32
+    lib.kda_fwd_check.argtypes = common + [i32, i32]
+    lib.kda_fwd_check.restype = i32
+    lib.kda_chunk_anchor.argtypes = [f32, i32]
+    lib.kda_chunk_anchor.restype = f32
+    lib.kda_status_string.argtypes = [i32]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def kda_status_string(status: int) -> str:
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def kda_chunk_anchor(lower_bound: float, chunk_size: int) -> float:
+    return float(load_library().kda_chunk_anchor(float(lower_bound), int(chunk_size)))
+
+
+def kda_fwd_check(*args) -> int:
+    """Host-only validation with raw integer pointers; same arguments as the C function."""
+    return int(load_library().kda_fwd_check(*args))
+
+
+def _state_dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KDA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return KDA_DTYPE_FP32
+    raise TypeError("state tensors must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def kda_fwd_sched(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                  initial_state=None, final_state=None, cu_seqlens=None,
+                  chunk_size: int = 0, v_tile: int = 0, stream=None) -> None:
+    """Runs the forward on the device tensors given (asynchronous on ``stream``).
+
+    q, k, v, g, out: bf16 ``[B,T,H,D]``; beta bf16 ``[B,T,H]``; A_log fp32 ``[H]``;
+    dt_bias fp32 ``[H,D]``; states ``[N,H,D,D]`` bf16 or fp32 (or None);
+    cu_seqlens int64 ``[N+1]`` on the device (varlen, B == 1) or None (batched).
+    ``stream`` defaults to torch's current stream on q's device.
+    """
+    import torch
+    lib = load_library()
+    acts = {"q": q, "k": k, "v": v, "g": g, "out": out}
+    for name, t in acts.items():
+        if t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise TypeError("%s must be a 4-d bfloat16 tensor" % name)
+    B, T, H, D = q.shape
+    for name, t in acts.items():
+        if tuple(t.shape) != (B, T, H, D):
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (B, T, H, D)))
+    if beta.dtype != torch.bfloat16 or tuple(beta.shape) != (B, T, H):
+        raise ValueError("beta must be bfloat16 [B,T,H]")
+    if A_log.dtype != torch.float32 or tuple(A_log.shape) != (H,):
+        raise ValueError("A_log must be float32 [H]")
+    if dt_bias.dtype != torch.float32 or tuple(dt_bias.shape) != (H, D):
+        raise ValueError("dt_bias must be float32 [H,D]")
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int64 or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-d int64 tensor")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    tensors = [q, k, v, g, beta, out, A_log, dt_bias]
+    for t in (initial_state, final_state, cu_seqlens):
+        if t is not None:
+            tensors.append(t)
+    for t in (initial_state, final_state):
+        if t is not None and tuple(t.shape) != (N, H, D, D):
+            raise ValueError("states must be [N,H,D,D] = %s" % ((N, H, D, D),))
+    dev = q.device
+    for t in tensors:
+        if t.device != dev or dev.type != "cuda":
+            raise ValueError("every tensor must live on the same GPU")
+        if not t.is_contiguous():
+            raise ValueError("every tensor must be contiguous")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    s_ptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib.kda_fwd_sched(
+        ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), float(scale), ptr(out), ptr(A_log),
+        ptr(dt_bias), float(lower_bound), ptr(initial_state),
+        _state_dtype_code(initial_state) if initial_state is not None else 0, ptr(final_state),
+        _state_dtype_code(final_state) if final_state is not None else 0, ptr(cu_seqlens), N, B,
+        T, H, D, s_ptr, int(chunk_size), int(v_tile))
+    if st != KDA_OK:
+        raise KdaError(st)
+
+
+def kda_fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None,
+            final_state=None, cu_seqlens=None, stream=None) -> None:
+    """The FlashKDA ``fwd`` contract with the library's automatic schedule."""
+    kda_fwd_sched(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                  final_state, cu_seqlens, 0, 0, stream)

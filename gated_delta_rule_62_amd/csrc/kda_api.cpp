@@ -1,0 +1,188 @@
+// Host side of the C ABI declared in include/kda.h: argument validation,
+// schedule selection and the kernel launch.  Nothing here touches device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/kda.h"
+#include "kda_params.h"
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;
+// Largest |base-2 exponent| a centred bf16 operand may need: 2^126 keeps every
+// scaled operand (|kh| <= 1, scale included) below the bf16 maximum.
+constexpr double kMaxRadius = 126.0;
+
+struct Range {
+  uintptr_t lo;
+  uintptr_t hi;  // exclusive
+};
+
+Range make_range(const void* p, int64_t bytes) {
+  Range r;
+  r.lo = reinterpret_cast<uintptr_t>(p);
+  r.hi = r.lo + (bytes > 0 ? static_cast<uintptr_t>(bytes) : 0);
+  return r;
+}
+
+bool overlaps(Range a, Range b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;  // empty ranges never overlap
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Exponent radius (base 2) of the centred chunk operands: (chunk / 2) * |lb| * log2(e).
+double chunk_radius(double lb, int chunk) { return 0.5 * chunk * std::fabs(lb) * kLog2e; }
+
+int auto_chunk(double lb) { return chunk_radius(lb, 32) <= kMaxRadius ? 32 : 16; }
+
+int auto_v_tile(int64_t D) { return static_cast<int>(D); }
+
+int resolve(const void* q, const void* k, const void* v, const void* g, const void* beta,
+            float scale, const void* out, const float* A_log, const float* dt_bias,
+            float lower_bound, const void* initial_state, int initial_state_dtype,
+            const void* final_state, int final_state_dtype, const int64_t* cu_seqlens,
+            int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t D, int chunk_size,
+            int v_tile, int* chunk_out, int* v_tile_out) {
+  if (!q || !k || !v || !g || !beta || !out || !A_log || !dt_bias) return KDA_ERR_NULL_ARG;
+  if (B < 1 || H < 1 || T < 0) return KDA_ERR_BAD_SHAPE;
+  if (T == 0 && cu_seqlens == nullptr) return KDA_ERR_BAD_SHAPE;
+  if (D != 32 && D != 64 && D != 128) return KDA_ERR_BAD_SHAPE;
+  if (H > (int64_t)1 << 24 || B * T > ((int64_t)1 << 40)) return KDA_ERR_BAD_SHAPE;
+  if (initial_state && initial_state_dtype != KDA_DTYPE_BF16 &&
+      initial_state_dtype != KDA_DTYPE_FP32)
+    return KDA_ERR_BAD_DTYPE;
+  if (final_state && final_state_dtype != KDA_DTYPE_BF16 && final_state_dtype != KDA_DTYPE_FP32)
+    return KDA_ERR_BAD_DTYPE;
+  if (cu_seqlens) {
+    if (B != 1 || num_seqs < 1) return KDA_ERR_BAD_VARLEN;
+  } else {
+    if (num_seqs != B) return KDA_ERR_BAD_VARLEN;
+  }
+  if (num_seqs * H > ((int64_t)1 << 31) / 4) return KDA_ERR_BAD_SHAPE;
+  if (!std::isfinite(scale)) return KDA_ERR_BAD_SCALE;
+  if (!std::isfinite(lower_bound) || !(lower_bound < 0.f)) return KDA_ERR_BAD_LOWER_BOUND;
+
+  int chunk = chunk_size;
+  if (chunk == 0) chunk = auto_chunk(lower_bound);
+  if (chunk != 16 && chunk != 32) return KDA_ERR_BAD_SCHEDULE;
+  if (chunk_radius(lower_bound, chunk) > kMaxRadius) return KDA_ERR_BAD_LOWER_BOUND;
+  int vt = v_tile == 0 ? auto_v_tile(D) : v_tile;
+  if (!kda::kda_schedule_supported(static_cast<int>(D), chunk, vt)) return KDA_ERR_BAD_SCHEDULE;
+
+  // Buffer extents and the aliasing contract.
+  const int64_t tok = B * T;
+  const int64_t act = tok * H * D * 2;
+  const int64_t st_elems = num_seqs * H * D * D;
+  const Range rq = make_range(q, act), rk = make_range(k, act), rv = make_range(v, act),
+              rg = make_range(g, act), rb = make_range(beta, tok * H * 2),
+              ra = make_range(A_log, H * 4), rd = make_range(dt_bias, H * D * 4),
+              rc = make_range(cu_seqlens, cu_seqlens ? (num_seqs + 1) * 8 : 0),
+              rs_in = make_range(initial_state,
+                                 initial_state ? st_elems * (initial_state_dtype ? 4 : 2) : 0),
+              rout = make_range(out, act),
+              rs_out = make_range(final_state,
+                                  final_state ? st_elems * (final_state_dtype ? 4 : 2) : 0);
+  const Range inputs_but_state[] = {rq, rk, rv, rg, rb, ra, rd, rc};
+  for (const Range& r : inputs_but_state) {
+    if (overlaps(rout, r) || overlaps(rs_out, r)) return KDA_ERR_BAD_ALIAS;
+  }
+  if (overlaps(rout, rs_in) || overlaps(rout, rs_out)) return KDA_ERR_BAD_ALIAS;
+  if (overlaps(rs_out, rs_in)) {
+    const bool exact = initial_state == final_state && initial_state_dtype == final_state_dtype;
+    if (!exact) return KDA_ERR_BAD_ALIAS;
+  }
+  *chunk_out = chunk;
+  *v_tile_out = vt;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_fwd_check(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                  float scale, const void* out, const float* A_log, const float* dt_bias,
+                  float lower_bound, const void* initial_state, int initial_state_dtype,
+                  const void* final_state, int final_state_dtype, const int64_t* cu_seqlens,
+                  int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t D, int chunk_size,
+                  int v_tile) {
+  int c = 0, vt = 0;
+  return resolve(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                 initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T,
+                 H, D, chunk_size, v_tile, &c, &vt);
+}
+
+int kda_fwd_sched(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                  float scale, void* out, const float* A_log, const float* dt_bias,
+                  float lower_bound, const void* initial_state, int initial_state_dtype,
+                  void* final_state, int final_state_dtype, const int64_t* cu_seqlens,
+                  int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t D, void* stream,
+                  int chunk_size, int v_tile) {
+  int chunk = 0, vt = 0;
+  const int st = resolve(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                         initial_state, initial_state_dtype, final_state, final_state_dtype,
+                         cu_seqlens, num_seqs, B, T, H, D, chunk_size, v_tile, &chunk, &vt);
+  if (st != KDA_OK) return st;
+
+  kda::KdaParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.g = static_cast<const uint16_t*>(g);
+  p.beta = static_cast<const uint16_t*>(beta);
+  p.out = static_cast<uint16_t*>(out);
+  p.A_log = A_log;
+  p.dt_bias = dt_bias;
+  p.s_in = initial_state;
+  p.s_out = final_state;
+  p.cu = cu_seqlens;
+  p.T = T;
+  p.T_total = B * T;
+  p.N = static_cast<int32_t>(num_seqs);
+  p.H = static_cast<int32_t>(H);
+  p.s_in_fp32 = initial_state_dtype == KDA_DTYPE_FP32 ? 1 : 0;
+  p.s_out_fp32 = final_state_dtype == KDA_DTYPE_FP32 ? 1 : 0;
+  p.n_vtiles = static_cast<int32_t>(D / vt);
+  p.scale = scale;
+  p.lb2 = static_cast<float>(lower_bound * kLog2e);
+  p.anchor = kda_chunk_anchor(lower_bound, chunk);
+  const hipError_t e =
+      kda::launch_kda_fwd(p, static_cast<int>(D), chunk, vt, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+            float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
+            const void* initial_state, int initial_state_dtype, void* final_state,
+            int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B,
+            int64_t T, int64_t H, int64_t D, void* stream) {
+  return kda_fwd_sched(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                       initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs,
+                       B, T, H, D, stream, 0, 0);
+}
+
+float kda_chunk_anchor(float lower_bound, int chunk_size) {
+  return static_cast<float>(0.5 * chunk_size * static_cast<double>(lower_bound) * kLog2e);
+}
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_NULL_ARG: return "KDA_ERR_NULL_ARG: a required pointer is NULL";
+    case KDA_ERR_BAD_SHAPE: return "KDA_ERR_BAD_SHAPE: unsupported sizes";
+    case KDA_ERR_BAD_DTYPE: return "KDA_ERR_BAD_DTYPE: unknown state dtype code";
+    case KDA_ERR_BAD_VARLEN: return "KDA_ERR_BAD_VARLEN: inconsistent cu_seqlens / num_seqs / B";
+    case KDA_ERR_BAD_ALIAS: return "KDA_ERR_BAD_ALIAS: buffers overlap beyond the exact state alias";
+    case KDA_ERR_BAD_LOWER_BOUND:
+      return "KDA_ERR_BAD_LOWER_BOUND: lower_bound must be finite, negative and inside the "
+             "chunk's bf16 exponent radius";
+    case KDA_ERR_BAD_SCALE: return "KDA_ERR_BAD_SCALE: scale must be finite";
+    case KDA_ERR_BAD_SCHEDULE: return "KDA_ERR_BAD_SCHEDULE: unsupported chunk size or value tile";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported an error";
+    default: return "KDA_ERR_UNKNOWN";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Internal launch parameters shared by the host API and the HIP kernels.
+#ifndef KDA_PARAMS_H_
+#define KDA_PARAMS_H_
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct KdaParams {
+  const uint16_t* q;        // bf16 [B*T, H, D]
+  const uint16_t* k;        // bf16 [B*T, H, D]
+  const uint16_t* v;        // bf16 [B*T, H, D]
+  const uint16_t* g;        // bf16 [B*T, H, D]
+  const uint16_t* beta;     // bf16 [B*T, H] (logits)
+  uint16_t* out;            // bf16 [B*T, H, D]
+  const float* A_log;       // [H]
+  const float* dt_bias;     // [H, D]
+  const void* s_in;         // [N, H, D, D] bf16/fp32 or nullptr
+  void* s_out;              // [N, H, D, D] bf16/fp32 or nullptr
+  const int64_t* cu;        // [N+1] or nullptr (batched)
+  int64_t T;                // tokens per batch row (batched mode)
+  int64_t T_total;          // B*T
+  int32_t N;                // sequences
+  int32_t H;                // heads
+  int32_t s_in_fp32;        // 1: initial state is fp32
+  int32_t s_out_fp32;       // 1: final state is fp32
+  int32_t n_vtiles;         // value tiles per (sequence, head)
+  float scale;              // output scale
+  float lb2;                // lower_bound * log2(e)
+  float anchor;             // fixed base-2 exponent anchor of the chunk
+};
+
+// Launches the fused forward for a resolved schedule; returns a hipError_t.
+hipError_t launch_kda_fwd(const KdaParams& p, int D, int chunk, int v_tile, hipStream_t stream);
+
+// Whether a (D, chunk, v_tile) schedule has a compiled kernel.
+bool kda_schedule_supported(int D, int chunk, int v_tile);
+
+}  // namespace kda
+
+#endif  // KDA_PARAMS_H_

@@ -1,0 +1,149 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) KDA recurrent prefill forward.
+ *
+ * The operation is the Kimi Delta Attention prefill forward described by the
+ * FlashInfer PR #4262 summary (section 1 "A Fused Recurrent-Prefill Kernel",
+ * section 2 "Chunk-32 Through Fixed-Anchor Exponent Centering", section 3
+ * "Intra-Chunk and Inter-Chunk Decomposition") with the call contract of
+ * FlashKDA's `fwd` ("How FlashKDA Manages Recurrent State Across Sequences and
+ * Batch Modes", the Python wrapper and both modes).  Per sequence n and head h
+ * the V x K state S evolves token by token as
+ *
+ *     lam_t = lower_bound * sigmoid(exp(A_log[h]) * (g_t + dt_bias[h]))  (per key column)
+ *     S     = S * diag(exp(lam_t))
+ *     S     = S + sigmoid(beta_t) * (v_t - S kh_t) kh_t^T
+ *     out_t = scale * S qh_t
+ *
+ * with qh, kh the L2-normalised q and k rows (x / sqrt(|x|^2 + 1e-6)).  The
+ * library evaluates this in chunks of 16 or 32 tokens with bf16 matrix-core
+ * products and an fp32 state that stays on chip for the whole sequence.
+ *
+ * Conventions for every entry point:
+ *   - Every pointer argument except `stream` is a caller-owned DEVICE pointer
+ *     to contiguous memory; the library never frees or retains it.
+ *   - The library allocates nothing and keeps no global state; calls on
+ *     different streams may run concurrently.
+ *   - kda_fwd is asynchronous: it validates on the host, enqueues one kernel on
+ *     `stream` and returns.  It never reads device memory on the host (in
+ *     particular not cu_seqlens) and never synchronises.
+ *   - Errors are returned as negative status codes; nothing aborts or throws
+ *     across this ABI.  On a validation error nothing is enqueued.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define KDA_OK 0
+#define KDA_ERR_NULL_ARG (-1)        /* a required pointer is NULL                      */
+#define KDA_ERR_BAD_SHAPE (-2)       /* B,T,H < 1 (T may be 0 only with cu_seqlens), or  */
+                                     /* D not in {32, 64, 128}                           */
+#define KDA_ERR_BAD_DTYPE (-3)       /* unknown state dtype code                         */
+#define KDA_ERR_BAD_VARLEN (-4)      /* cu_seqlens with B != 1, num_seqs < 1, or         */
+                                     /* num_seqs != B without cu_seqlens                 */
+#define KDA_ERR_BAD_ALIAS (-5)       /* an output overlaps an input or the other output; */
+                                     /* only the exact in-place state alias is allowed   */
+#define KDA_ERR_BAD_LOWER_BOUND (-6) /* lower_bound not finite, not < 0, or beyond the   */
+                                     /* bf16 exponent-safe radius of the chunk size      */
+#define KDA_ERR_BAD_SCALE (-7)       /* scale not finite                                 */
+#define KDA_ERR_BAD_SCHEDULE (-8)    /* unsupported forced chunk size or value tile      */
+#define KDA_ERR_HIP (-9)             /* the HIP runtime reported an error at launch      */
+
+/* State dtype codes (initial_state_dtype, final_state_dtype). */
+#define KDA_DTYPE_BF16 0
+#define KDA_DTYPE_FP32 1
+
+/*
+ * kda_fwd -- the prefill forward (FlashKDA `fwd` contract: q, k, v, g, beta,
+ * scale, out, A_log, dt_bias, lower_bound, initial_state, final_state,
+ * cu_seqlens).
+ *
+ *   q, k, v, g     bf16 [B, T, H, D], contiguous (D fastest).  K = V = D.
+ *   beta           bf16 [B, T, H], logits (the kernel applies the sigmoid).
+ *   scale          output scale, folded into the normalised q; finite.
+ *   out            bf16 [B, T, H, D], written for every token (padding-free).
+ *   A_log          fp32 [H].
+ *   dt_bias        fp32 [H, D].
+ *   lower_bound    gate lower bound lb (finite, < 0); per-token decay lies in (lb, 0).
+ *   initial_state  [num_seqs, H, D(v), D(k)] of initial_state_dtype, or NULL for zeros.
+ *   final_state    [num_seqs, H, D(v), D(k)] of final_state_dtype, or NULL (not written).
+ *                  It may be exactly the same allocation as initial_state (same
+ *                  pointer and dtype: in-place update); any other overlap between
+ *                  buffers is rejected.  Each workgroup reads all state rows it
+ *                  owns before it writes any of them, which makes the alias safe.
+ *   cu_seqlens     int64 [num_seqs + 1] device array, or NULL.
+ *                  NULL: batched mode, num_seqs == B, sequence b is tokens
+ *                  [b*T, (b+1)*T) of the flattened [B*T] axis, no resets.
+ *                  Non-NULL: varlen mode, B == 1, sequence n is tokens
+ *                  [cu[n], cu[n+1]); the state restarts from initial_state[n]
+ *                  (or zeros) at every sequence.  Preconditions (not checked on
+ *                  the host, which never reads device memory): cu[0] = 0,
+ *                  non-decreasing, cu[num_seqs] = T.  The kernel clamps every
+ *                  index into [0, T] so a malformed array cannot make it access
+ *                  memory out of bounds; results are then unspecified.
+ *                  An empty sequence passes its initial state (or zeros) through.
+ *   num_seqs       N (see above).
+ *   B, T, H, D     sizes; D in {32, 64, 128}.
+ *   stream         a hipStream_t (NULL: the null stream).
+ *
+ * Returns KDA_OK or a negative status.  lower_bound must satisfy
+ * |lower_bound| * log2(e) * 8 <= 126 (|lb| <= 10.92); the library uses 32-token
+ * chunks when |lb| * log2(e) * 16 <= 126 (|lb| <= 5.458) and 16-token chunks
+ * otherwise, each centred on the fixed anchor (chunk/2) * lb * log2(e).
+ */
+int kda_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+            float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
+            const void* initial_state, int initial_state_dtype, void* final_state,
+            int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B,
+            int64_t T, int64_t H, int64_t D, void* stream);
+
+/*
+ * kda_fwd_sched -- kda_fwd with a forced schedule, for tests and tuning.
+ *   chunk_size  0 (automatic), 16 or 32.  32 is rejected (KDA_ERR_BAD_LOWER_BOUND)
+ *               when |lb| > 5.458.
+ *   v_tile      0 (automatic) or the number of value rows one workgroup owns:
+ *               a divisor of D that is a multiple of 16 and at least 32
+ *               (KDA_ERR_BAD_SCHEDULE otherwise).
+ * Everything else is exactly as kda_fwd.
+ */
+int kda_fwd_sched(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                  float scale, void* out, const float* A_log, const float* dt_bias,
+                  float lower_bound, const void* initial_state, int initial_state_dtype,
+                  void* final_state, int final_state_dtype, const int64_t* cu_seqlens,
+                  int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t D, void* stream,
+                  int chunk_size, int v_tile);
+
+/*
+ * kda_fwd_check -- the host-side validation of kda_fwd_sched on its own: the
+ * same arguments without the stream, returns the status kda_fwd_sched would
+ * return before launching.  Pure host code (pointer values are compared, never
+ * dereferenced); needs no GPU.
+ */
+int kda_fwd_check(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                  float scale, const void* out, const float* A_log, const float* dt_bias,
+                  float lower_bound, const void* initial_state, int initial_state_dtype,
+                  const void* final_state, int final_state_dtype, const int64_t* cu_seqlens,
+                  int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t D, int chunk_size,
+                  int v_tile);
+
+/*
+ * kda_chunk_anchor -- the fixed exponent anchor (base 2) used for a chunk size:
+ * (chunk_size / 2) * lower_bound * log2(e).  For 32-token chunks this is the
+ * anchor 16 * lower_bound * log2(e) of section 2 of the PR #4262 summary
+ * (about -115.42 for lower_bound = -5).  Pure host function.
+ */
+float kda_chunk_anchor(float lower_bound, int chunk_size);
+
+/* kda_status_string -- a static, human-readable name for a status code. */
+const char* kda_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,145 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and its
+host-side validation returns the documented status codes (no GPU call is made:
+kda_fwd_check only compares pointer values and sizes)."""
+from __future__ import annotations
+
+import json
+import math
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_62_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.library_path()):
+        kda.build()
+    return kda.load_library()
+
+
+def _declared_functions():
+    names = []
+    for hdr in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if hdr.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", hdr)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w\s\*]*?\b(kda_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert {"kda_fwd", "kda_fwd_sched", "kda_fwd_check", "kda_chunk_anchor",
+            "kda_status_string"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(0, -10, -1):
+        s = kda.kda_status_string(code)
+        assert s.startswith("KDA_")
+    assert "UNKNOWN" in kda.kda_status_string(-1234)
+
+
+def test_anchor_matches_printed_value(lib):
+    with open(os.path.join(ROOT, "tests", "golden", "anchor_constants.json")) as f:
+        gold = json.load(f)
+    a = kda.kda_chunk_anchor(gold["lower_bound"], gold["chunk"])
+    assert round(a, gold["anchor_decimals"]) == gold["anchor_printed"]
+    assert abs(kda.kda_chunk_anchor(-5.0, 16) - a / 2) < 1e-4
+
+
+# fake device addresses, far apart so that only deliberate overlaps overlap
+GB = 1 << 30
+
+
+def _args(B=2, T=64, H=4, D=128, N=None, has_cu=False, has_s_in=True, has_s_out=True, in_dt=0,
+          out_dt=0, lb=-5.0, scale=None, chunk=0, vt=0, **over):
+    N = B if N is None else N
+    base = dict(q=1 * GB, k=2 * GB, v=3 * GB, g=4 * GB, beta=5 * GB, out=6 * GB, A_log=7 * GB,
+                dt_bias=8 * GB, s_in=9 * GB if has_s_in else None,
+                s_out=10 * GB if has_s_out else None, cu=11 * GB if has_cu else None)
+    base.update(over)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    return (base["q"], base["k"], base["v"], base["g"], base["beta"], scale, base["out"],
+            base["A_log"], base["dt_bias"], lb, base["s_in"], in_dt, base["s_out"], out_dt,
+            base["cu"], N, B, T, H, D, chunk, vt)
+
+
+def _check(**kw):
+    return kda.kda_fwd_check(*_args(**kw))
+
+
+def test_valid_calls(lib):
+    assert _check() == kda.KDA_OK
+    assert _check(has_s_in=False, has_s_out=False) == kda.KDA_OK
+    assert _check(B=1, T=2024, N=3, has_cu=True, in_dt=1, out_dt=1) == kda.KDA_OK
+    assert _check(B=1, T=0, N=3, has_cu=True) == kda.KDA_OK  # every sequence empty
+    for D in (32, 64, 128):
+        assert _check(D=D) == kda.KDA_OK
+    assert _check(chunk=16) == kda.KDA_OK and _check(chunk=32) == kda.KDA_OK
+    assert _check(vt=64) == kda.KDA_OK
+
+
+def test_null_and_shape_errors(lib):
+    for name in ("q", "k", "v", "g", "beta", "out", "A_log", "dt_bias"):
+        assert _check(**{name: None}) == kda.KDA_ERR_NULL_ARG, name
+    assert _check(B=0) == kda.KDA_ERR_BAD_SHAPE
+    assert _check(H=0) == kda.KDA_ERR_BAD_SHAPE
+    assert _check(T=0) == kda.KDA_ERR_BAD_SHAPE
+    assert _check(T=-1) == kda.KDA_ERR_BAD_SHAPE
+    for D in (16, 48, 96, 256):
+        assert _check(D=D) == kda.KDA_ERR_BAD_SHAPE
+
+
+def test_dtype_and_varlen_errors(lib):
+    assert _check(in_dt=2) == kda.KDA_ERR_BAD_DTYPE
+    assert _check(out_dt=-1) == kda.KDA_ERR_BAD_DTYPE
+    assert _check(has_cu=True, B=2, N=3) == kda.KDA_ERR_BAD_VARLEN
+    assert _check(has_cu=True, B=1, N=0) == kda.KDA_ERR_BAD_VARLEN
+    assert _check(N=3) == kda.KDA_ERR_BAD_VARLEN  # batched needs N == B
+
+
+def test_scalar_errors(lib):
+    for lb in (0.0, 1.0, float("nan"), float("inf"), float("-inf")):
+        assert _check(lb=lb) == kda.KDA_ERR_BAD_LOWER_BOUND, lb
+    assert _check(scale=float("nan")) == kda.KDA_ERR_BAD_SCALE
+    # exponent-safe radius: 32-token chunks to |lb| = 126 / (16 log2 e) = 5.458...,
+    # 16-token chunks to 10.91...; the automatic schedule falls back to 16.
+    assert _check(lb=-5.45, chunk=32) == kda.KDA_OK
+    assert _check(lb=-5.47, chunk=32) == kda.KDA_ERR_BAD_LOWER_BOUND
+    assert _check(lb=-5.47) == kda.KDA_OK
+    assert _check(lb=-10.9) == kda.KDA_OK
+    assert _check(lb=-10.95) == kda.KDA_ERR_BAD_LOWER_BOUND
+
+
+def test_schedule_errors(lib):
+    assert _check(chunk=8) == kda.KDA_ERR_BAD_SCHEDULE
+    assert _check(chunk=64) == kda.KDA_ERR_BAD_SCHEDULE
+    assert _check(vt=48) == kda.KDA_ERR_BAD_SCHEDULE
+    assert _check(vt=16) == kda.KDA_ERR_BAD_SCHEDULE
+    assert _check(D=32, vt=64) == kda.KDA_ERR_BAD_SCHEDULE
+
+
+def test_alias_contract(lib):
+    # exact in-place alias: same pointer and dtype
+    assert _check(s_out=9 * GB) == kda.KDA_OK
+    # same pointer, different dtype: partial overlap of extents
+    assert _check(s_out=9 * GB, out_dt=1) == kda.KDA_ERR_BAD_ALIAS
+    # partial overlap of the two states
+    assert _check(s_out=9 * GB + 256) == kda.KDA_ERR_BAD_ALIAS
+    # out overlapping an input, or the final state overlapping an input
+    assert _check(out=1 * GB + 2) == kda.KDA_ERR_BAD_ALIAS
+    assert _check(out=9 * GB) == kda.KDA_ERR_BAD_ALIAS
+    assert _check(s_out=3 * GB) == kda.KDA_ERR_BAD_ALIAS
+    assert _check(s_out=6 * GB) == kda.KDA_ERR_BAD_ALIAS
+    assert _check(B=1, T=100, N=2, has_cu=True, s_out=11 * GB) == kda.KDA_ERR_BAD_ALIAS
+    # adjacent, non-overlapping buffers are fine: q ends where k starts
+    act = 2 * 64 * 4 * 128 * 2
+    assert _check(k=1 * GB + act) == kda.KDA_OK

@@ -1,0 +1,218 @@
+"""GPU parity: the HIP library against the fp64 CPU oracle, element by element.
+
+Tolerances (stated up front for bf16 inputs and outputs): for ``out`` and for
+``final_state``, max-abs error <= 2e-2 and relative L2 error
+||x - x_ref||_2 / ||x_ref||_2 <= 5e-3, both computed in fp64 over the whole
+tensor compared.  Every call goes through the C ABI (``kda_fwd`` /
+``kda_fwd_sched``) via the package binding.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_62_amd as kda
+import oracle
+from gated_delta_rule_62_amd.workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+REL_L2 = 5e-3
+DEV = "cuda"
+
+
+def _errors(x, ref):
+    x = x.detach().to("cpu", torch.float64).numpy() if hasattr(x, "detach") else x
+    d = np.abs(x - ref)
+    rel = np.linalg.norm(x - ref) / max(np.linalg.norm(ref), 1e-300)
+    return float(d.max()) if d.size else 0.0, float(rel)
+
+
+def _assert_close(x, ref, what):
+    mx, rel = _errors(x, ref)
+    print("%s: max-abs %.3e rel-L2 %.3e" % (what, mx, rel), flush=True)
+    assert mx <= MAX_ABS and rel <= REL_L2, "%s: max-abs %.3e rel-L2 %.3e" % (what, mx, rel)
+
+
+def _run(inp, chunk=0, vt=0, final=True):
+    kda.kda_fwd_sched(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"],
+                      inp["out"], inp["A_log"], inp["dt_bias"], inp["lower_bound"],
+                      inp["initial_state"], inp["final_state"] if final else None,
+                      inp["cu_seqlens"], chunk_size=chunk, v_tile=vt)
+    torch.cuda.synchronize()
+
+
+def _oracle(inp, heads=None):
+    sel = (lambda t: t) if heads is None else (lambda t: t[:, :, heads])
+    s0 = inp["initial_state"]
+    if s0 is not None and heads is not None:
+        s0 = s0[:, heads]
+    A_log = inp["A_log"] if heads is None else inp["A_log"][heads]
+    dt_bias = inp["dt_bias"] if heads is None else inp["dt_bias"][heads]
+    return oracle.kda_fwd(sel(inp["q"]), sel(inp["k"]), sel(inp["v"]), sel(inp["g"]),
+                          sel(inp["beta"]), inp["scale"], A_log, dt_bias, inp["lower_bound"],
+                          s0, inp["cu_seqlens"])
+
+
+def _check_against_oracle(inp, chunk=0, vt=0, tag=""):
+    _run(inp, chunk, vt)
+    out_ref, fin_ref = _oracle(inp)
+    _assert_close(inp["out"], out_ref, tag + " out")
+    _assert_close(inp["final_state"], fin_ref, tag + " final_state")
+
+
+# --------------------------------------------------------------------------
+# the five workloads at full size, in the launch configuration the benchmark uses
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["small", "batched", "varlen3", "many"])
+def test_workload_full(name):
+    w = WORKLOADS[name]
+    print("workload %s" % name, flush=True)
+    inp = make_inputs(w, device=DEV)
+    _check_against_oracle(inp, chunk=w.chunk_size, tag=name)
+
+
+def test_workload_long_sampled_heads():
+    # T = 32768, H = 96: the whole launch runs on the GPU; the oracle recomputes a
+    # sample of heads (each a full 32768-token recurrence) for comparison.
+    w = WORKLOADS["long"]
+    inp = make_inputs(w, device=DEV)
+    _run(inp)
+    heads = [0, 41, 95]
+    out_ref, fin_ref = _oracle(inp, heads=heads)
+    _assert_close(inp["out"][:, :, heads], out_ref, "long out (heads %s)" % heads)
+    _assert_close(inp["final_state"][:, heads], fin_ref, "long final_state (heads %s)" % heads)
+
+
+# --------------------------------------------------------------------------
+# schedules and shapes at sizes the oracle finishes in well under a second
+# --------------------------------------------------------------------------
+
+SCHEDULES = [(128, 32, 128), (128, 16, 128), (128, 32, 64), (128, 16, 64), (64, 32, 64),
+             (64, 16, 64), (64, 32, 32), (64, 16, 32), (32, 32, 32), (32, 16, 32)]
+
+
+@pytest.mark.parametrize("D,chunk,vt", SCHEDULES)
+def test_schedules_ragged(D, chunk, vt):
+    w = Workload("sched", B=2, T=77, H=3, D=D, seed=100 + D + chunk + vt, state_in="bf16")
+    inp = make_inputs(w, device=DEV)
+    _check_against_oracle(inp, chunk, vt, tag="D%d C%d VT%d" % (D, chunk, vt))
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_varlen_edge_lengths_fp32_state(chunk):
+    # empty, length-1, exact-chunk and ragged sequences, fp32 state in and out
+    w = Workload("edges", B=1, T=0, H=4, D=128, seed=7, lengths=[0, 1, 17, 32, 64, 0, 5, 100],
+                 state_in="fp32", state_out="fp32")
+    inp = make_inputs(w, device=DEV)
+    _check_against_oracle(inp, chunk, tag="edges C%d" % chunk)
+    # empty sequences pass their state through unchanged
+    for n in (0, 5):
+        assert torch.equal(inp["final_state"][n], inp["initial_state"][n])
+
+
+def test_no_initial_state_and_no_final_state():
+    w = Workload("nostate", B=1, T=200, H=2, D=128, seed=8, state_in=None)
+    inp = make_inputs(w, device=DEV)
+    _check_against_oracle(inp, tag="zeros-in")
+    out_first = inp["out"].clone()
+    inp["out"].fill_(float("nan"))
+    _run(inp, final=False)
+    assert torch.equal(inp["out"], out_first)
+
+
+def test_bf16_in_fp32_out_and_fp32_in_bf16_out():
+    for s_in, s_out in (("bf16", "fp32"), ("fp32", "bf16")):
+        w = Workload("mix", B=2, T=90, H=2, D=64, seed=9, state_in=s_in, state_out=s_out)
+        inp = make_inputs(w, device=DEV)
+        _check_against_oracle(inp, tag="state %s->%s" % (s_in, s_out))
+
+
+def test_strong_lower_bound_uses_16_token_chunks():
+    w = Workload("lb8", B=1, T=150, H=2, D=128, seed=10, lower_bound=-8.0)
+    inp = make_inputs(w, device=DEV)
+    _check_against_oracle(inp, tag="lb=-8")
+
+
+def test_weak_decay():
+    w = Workload("lb01", B=1, T=300, H=2, D=128, seed=11, lower_bound=-0.1)
+    inp = make_inputs(w, device=DEV)
+    _check_against_oracle(inp, tag="lb=-0.1")
+
+
+def test_projection_property_on_gpu():
+    # beta logit +30 (sigmoid rounds to 1 in fp32) and q = k: out_t = scale v_t for
+    # every token whatever the gates and state; checked at bf16 output precision.
+    w = Workload("proj", B=1, T=100, H=2, D=128, seed=12, state_in="bf16")
+    inp = make_inputs(w, device=DEV)
+    inp["beta"].fill_(30.0)
+    inp["q"].copy_(inp["k"])
+    _run(inp)
+    want = (inp["scale"] * inp["v"].double())
+    got = inp["out"].double()
+    err = (got - want).abs().max().item()
+    print("projection max-abs %.3e (|scale v| max %.3e)" % (err, want.abs().max().item()))
+    assert err <= 2e-2 * want.abs().max().item()
+
+
+# --------------------------------------------------------------------------
+# hygiene: in-place alias, full overwrite, guard bands, determinism
+# --------------------------------------------------------------------------
+
+def test_exact_inplace_alias_matches_separate_buffers():
+    w = Workload("alias", B=2, T=130, H=3, D=128, seed=13, state_in="bf16")
+    inp = make_inputs(w, device=DEV)
+    _run(inp)
+    sep_out, sep_fin = inp["out"].clone(), inp["final_state"].clone()
+    state = inp["initial_state"].clone()
+    kda.kda_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"], inp["out"],
+                inp["A_log"], inp["dt_bias"], inp["lower_bound"], state, state, None)
+    torch.cuda.synchronize()
+    assert torch.equal(inp["out"], sep_out) and torch.equal(state, sep_fin)
+
+
+def test_outputs_fully_overwritten_and_guard_bands_intact():
+    w = Workload("guard", B=1, T=0, H=3, D=128, seed=14, lengths=[40, 0, 77],
+                 state_in="bf16")
+    inp = make_inputs(w, device=DEV)
+    guard = 4096
+    out_n = inp["out"].numel()
+    fin_n = inp["final_state"].numel()
+    out_buf = torch.full((out_n + 2 * guard,), 7.0, dtype=torch.bfloat16, device=DEV)
+    fin_buf = torch.full((fin_n + 2 * guard,), 7.0, dtype=torch.bfloat16, device=DEV)
+    out_buf[guard:guard + out_n] = float("nan")
+    fin_buf[guard:guard + fin_n] = float("nan")
+    inp["out"] = out_buf[guard:guard + out_n].view(inp["out"].shape)
+    inp["final_state"] = fin_buf[guard:guard + fin_n].view(inp["final_state"].shape)
+    _check_against_oracle(inp, tag="guard")
+    assert not torch.isnan(inp["out"]).any() and not torch.isnan(inp["final_state"]).any()
+    for buf, n in ((out_buf, out_n), (fin_buf, fin_n)):
+        assert torch.all(buf[:guard] == 7.0) and torch.all(buf[guard + n:] == 7.0)
+
+
+def test_bitwise_deterministic():
+    w = Workload("det", B=1, T=0, H=8, D=128, seed=15, lengths=[500, 3, 260], state_in="bf16")
+    inp = make_inputs(w, device=DEV)
+    _run(inp)
+    ref = (inp["out"].clone(), inp["final_state"].clone())
+    for _ in range(2):
+        inp["out"].zero_()
+        inp["final_state"].zero_()
+        _run(inp)
+        assert torch.equal(inp["out"], ref[0]) and torch.equal(inp["final_state"], ref[1])
+
+
+def test_invalid_arguments_raise_before_launch():
+    w = Workload("bad", B=1, T=16, H=1, D=128, seed=16)
+    inp = make_inputs(w, device=DEV)
+    with pytest.raises(kda.KdaError):
+        kda.kda_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"],
+                    inp["out"], inp["A_log"], inp["dt_bias"], 0.5)
+    with pytest.raises(kda.KdaError):
+        kda.kda_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"], inp["q"],
+                    inp["A_log"], inp["dt_bias"], -5.0)
