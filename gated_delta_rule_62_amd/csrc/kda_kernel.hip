@@ -29,7 +29,11 @@
 //   pi_g = {32s + 4g + i} U {32s + 16 + 4g + i},  i < 4,
 // and the A operands read from LDS use the same permutation, so the product is
 // exact whatever order the hardware reduces in.  The same holds for the C-long
-// reductions (U, the state update and the output) with the chunk tiles.
+// reductions (U, the state update and the output) with the chunk tiles; with
+// 16-token chunks the upper four slots of both operands are zero.  Every bf16
+// product uses the one 16x16x32 shape: a 16x16x16 MFMA that accumulates onto
+// a 16x16x32 result was observed to read part of that accumulator before the
+// first instruction had written it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,7 +44,6 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
@@ -64,10 +67,6 @@ __device__ __forceinline__ u16 to_bf16(float x) { return (u16)(pack_bf16(x, 0.f)
 __device__ __forceinline__ f32x4_t mfma_k32(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mfma_k16(u32x2_t a, u32x2_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
-                                                   __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -176,8 +175,16 @@ __device__ __forceinline__ u32x4_t acc_pair_to_b(f32x4_t t0, f32x4_t t1) {
                pack_bf16(t1[2], t1[3])};
   return r;
 }
-__device__ __forceinline__ u32x2_t acc_to_b(f32x4_t t0) {
-  u32x2_t r = {pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3])};
+// One accumulator tile (rows 4g+i of a 16-row block) -> bf16 B operand whose
+// reduction slots 4-7 are zero.
+__device__ __forceinline__ u32x4_t acc_to_b_pad(f32x4_t t0) {
+  u32x4_t r = {pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]), 0u, 0u};
+  return r;
+}
+// A operand for a 16-long reduction: row r, columns 4g .. 4g+3, slots 4-7 zero.
+__device__ __forceinline__ u32x4_t lds_a_pad(const u16* row, int g) {
+  u32x2_t lo = *reinterpret_cast<const u32x2_t*>(row + 4 * g);
+  u32x4_t r = {lo[0], lo[1], 0u, 0u};
   return r;
 }
 
@@ -517,29 +524,31 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
           for (int nt = 0; nt < F::NTW; ++nt) O[ct][nt] = mfma_k32(aM, bU[nt], O[ct][nt]);
         }
       } else {
-        u32x2_t bR[F::NTW];
+        // 16-token chunks: the same 16x16x32 instruction with reduction slots 4-7
+        // zero in both operands (one MFMA shape on every accumulator chain).
+        u32x4_t bR[F::NTW];
 #pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt) bR[nt] = acc_to_b(P[0][nt]);
-        const u32x2_t aI = *reinterpret_cast<const u32x2_t*>(&sm.INV[l16][4 * lg]);
+        for (int nt = 0; nt < F::NTW; ++nt) bR[nt] = acc_to_b_pad(P[0][nt]);
+        const u32x4_t aI = lds_a_pad(&sm.INV[l16][0], lg);
 #pragma unroll
         for (int nt = 0; nt < F::NTW; ++nt)
-          U[0][nt] = mfma_k16(aI, bR[nt], f32x4_t{0.f, 0.f, 0.f, 0.f});
-        u32x2_t bU[F::NTW];
+          U[0][nt] = mfma_k32(aI, bR[nt], f32x4_t{0.f, 0.f, 0.f, 0.f});
+        u32x4_t bU[F::NTW];
 #pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt) bU[nt] = acc_to_b(U[0][nt]);
+        for (int nt = 0; nt < F::NTW; ++nt) bU[nt] = acc_to_b_pad(U[0][nt]);
 #pragma unroll
         for (int kt = 0; kt < F::KT; ++kt) {
           f32x4_t av = *reinterpret_cast<const f32x4_t*>(&sm.a[16 * kt + 4 * lg]);
-          const u32x2_t aR = *reinterpret_cast<const u32x2_t*>(&sm.KrT[16 * kt + l16][4 * lg]);
+          const u32x4_t aR = lds_a_pad(&sm.KrT[16 * kt + l16][0], lg);
 #pragma unroll
           for (int nt = 0; nt < F::NTW; ++nt) {
             S[kt][nt] = S[kt][nt] * av;
-            S[kt][nt] = mfma_k16(aR, bU[nt], S[kt][nt]);
+            S[kt][nt] = mfma_k32(aR, bU[nt], S[kt][nt]);
           }
         }
-        const u32x2_t aM = *reinterpret_cast<const u32x2_t*>(&sm.Mqk[l16][4 * lg]);
+        const u32x4_t aM = lds_a_pad(&sm.Mqk[l16][0], lg);
 #pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt) O[0][nt] = mfma_k16(aM, bU[nt], O[0][nt]);
+        for (int nt = 0; nt < F::NTW; ++nt) O[0][nt] = mfma_k32(aM, bU[nt], O[0][nt]);
       }
 
       // store O^T -> out[token, h, value] (bf16)
