@@ -114,6 +114,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=24,
                     help="heads of the workload the CPU oracle baseline runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (a known-size "
+                         "kernel for scaling HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -184,6 +187,14 @@ def main():
                      "algorithmic_bytes": nbytes, "counted_tflops": tflops},
         "kernel_source_hash": kernel_source_hash(),
     }
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes"] = {"read": n * 4, "write": n * 4}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_heads)
     print(json.dumps(result), flush=True)

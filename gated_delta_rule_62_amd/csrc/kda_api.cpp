@@ -49,7 +49,8 @@ int resolve(const void* q, const void* k, const void* v, const void* g, const vo
   if (B < 1 || H < 1 || T < 0) return KDA_ERR_BAD_SHAPE;
   if (T == 0 && cu_seqlens == nullptr) return KDA_ERR_BAD_SHAPE;
   if (D != 32 && D != 64 && D != 128) return KDA_ERR_BAD_SHAPE;
-  if (H > (int64_t)1 << 24 || B * T > ((int64_t)1 << 40)) return KDA_ERR_BAD_SHAPE;
+  // the kernels address one chunk (up to 32 token rows) with 32-bit byte offsets
+  if (H * D * 2 * 32 >= ((int64_t)1 << 31) || B * T > ((int64_t)1 << 40)) return KDA_ERR_BAD_SHAPE;
   if (initial_state && initial_state_dtype != KDA_DTYPE_BF16 &&
       initial_state_dtype != KDA_DTYPE_FP32)
     return KDA_ERR_BAD_DTYPE;

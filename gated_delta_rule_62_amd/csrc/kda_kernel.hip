@@ -21,6 +21,19 @@
 //        P^T = Kd S^T, O0^T = Qd S^T, R^T = diag(beta)(V - P^T), U^T = INV R^T,
 //        S^T <- diag(a) S^T + Kr^T U^T,  O^T = O0^T + Mqk U^T
 //
+// Schedule.  Steps 1-5 only touch chunk-local data, step 6 is the strictly
+// ordered recurrence (section 3's scheduling property).  Step s of the main
+// loop runs the state side of chunk s next to the preparation of chunk s+1,
+// in four phases separated by workgroup barriers that fence LDS only, so the
+// raw inputs of chunk s+2, loaded into registers during step s, stay in flight
+// across them:
+//   A  gate and norms of s+1 (VALU)     | P, O0 of s (MFMA) | X21 of s (wave 0)
+//   B  prefix scan of s+1               | R, U, state update, output of s
+//   C  exponent-scaled operands of s+1  | coalesced store of the output of s
+//   D  L, Mqk and diagonal inverse blocks of s+1
+// Two LDS slots hold the prepared operands of chunks s and s+1 (the page's
+// prep ring, two deep here).
+//
 // Layout of the state in registers.  Each wave holds S^T (K rows x its value
 // columns) as 16x16 fp32 accumulator tiles: lane l owns value column (l & 15)
 // and key rows 4*(l >> 4) + i, i < 4.  An accumulator tile pair (key rows
@@ -48,6 +61,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -72,6 +86,19 @@ __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Workgroup barrier that orders LDS only: outstanding global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+// Makes one wave's LDS writes visible to the other lanes of the same wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 __device__ __forceinline__ float fast_sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
 }
@@ -87,77 +114,88 @@ struct Cfg {
   static constexpr int KS = D / 32;            // 32-wide steps of D-long reductions
   static constexpr int CT = C / 16;            // 16-row chunk tiles
   static constexpr int NTW = VT / (16 * NW);   // 16-column value tiles per wave
-  static constexpr int EPT = C * D / NTHR;     // row-layout elements per thread
+  static constexpr int EPT = C * D / NTHR;     // row-layout elements per thread (q, k, g)
   static constexpr int TPR = D / EPT;          // threads per chunk row
-  static constexpr int NGRP = NTHR / D;        // row groups of the column-layout scan
-  static constexpr int RPG = C / NGRP;         // rows per scan group
+  static constexpr int EPV = C * VT / NTHR;    // row-layout elements per thread (v)
+  static constexpr int TPRV = VT / EPV;        // threads per value row
+  static constexpr int SCOLS = D / NW;         // scan columns per wave
+  static constexpr int SPASS = SCOLS / 16;     // scan passes (16 columns x 4 row groups)
+  static constexpr int RPG = C / 4;            // rows per scan group
   static constexpr int LDQ = D + 8;            // bf16 row stride of [C][D] tiles
-  static constexpr int LDKT = C + 8;           // bf16 row stride of the [D][C] Kr^T tile
+  static constexpr int LDG = D + 4;            // fp32 row stride of the prefix tile
+  static constexpr int LDR = D + 16;           // bf16 row stride of the [C][D] Kr tile
   static constexpr int LDC = C + 8;            // bf16 row stride of [C][C] tiles
-  static constexpr int LDV = VT + 8;           // bf16 row stride of the [C][VT] value tile
+  static constexpr int LDV = VT + 8;           // bf16 row stride of [C][VT] value tiles
   static constexpr int LDL = C + 4;            // fp32 row stride of [C][C] tiles
   static_assert(C == 16 || C == 32, "chunk");
   static_assert(NTW >= 1 && NTW * 16 * NW == VT, "value tiling");
   static_assert(EPT == 4 || EPT == 8 || EPT == 16, "row layout");
-  static_assert(TPR <= 64 && (64 % TPR) == 0, "row reduction stays inside a wave");
-  static_assert(NGRP >= 1 && C % NGRP == 0, "scan layout");
+  static_assert(EPV == 4 || EPV == 8 || EPV == 16, "value row layout");
+  static_assert(TPR >= 2 && TPR <= 32, "row reduction: DPP inside rows, one cross-row step");
+  static_assert(SPASS >= 1 && SPASS * 16 * NW == D, "scan layout");
   static_assert(D % 32 == 0, "head dim");
+  static_assert(NW >= 2, "two waves for the diagonal inverse blocks");
+};
+
+// Prepared operands of one chunk.
+template <class F>
+struct alignas(16) Slot {
+  u16 Qd[F::C][F::LDQ];
+  u16 Kd[F::C][F::LDQ];
+  u16 Kr[F::C][F::LDR];
+  u16 INV[F::C][F::LDC];
+  u16 Mqk[F::C][F::LDC];
+  u16 V[F::C][F::LDV];
+  float a[2 * F::D];         // 2^G_T (second half: discarded writes)
+  float beta[F::NTHR];       // sigmoid(beta); entries past the chunk rows unused
 };
 
 template <class F>
 struct alignas(16) Smem {
-  u16 Qc[F::C][F::LDQ];
+  Slot<F> slot[2];
+  u16 Qc[F::C][F::LDQ];      // centred operands of the chunk being prepared
   u16 Kc[F::C][F::LDQ];
   u16 Ki[F::C][F::LDQ];
-  u16 Qd[F::C][F::LDQ];
-  u16 Kd[F::C][F::LDQ];
-  u16 KrT[F::D][F::LDKT];
-  u16 V[F::C][F::LDV];
-  u16 INV[F::C][F::LDC];
-  u16 Mqk[F::C][F::LDC];
-  float G[F::C][F::D];       // base-2 decay, then its inclusive prefix
+  u16 Ost[F::C][F::LDV];     // output staging for coalesced stores
+  float G[F::C][F::LDG];     // base-2 decay, then its inclusive prefix
   float L[F::C][F::LDL];     // strictLower(diag(beta) Kc Ki^T)
-  float X[F::C][F::LDL];     // fp32 (I + L)^-1
+  float X[F::C][F::LDL];     // fp32 (I + L)^-1 diagonal blocks
   float Y[16][17];           // L21 X11 of the blocked inverse
-  float tot[F::NGRP][F::D];  // scan group totals
-  float a[F::D];             // 2^G_T
-  float gtc[F::D];           // 2^(G_T - Ca)
-  float beta[F::C];          // sigmoid(beta)
+  float gtc[2 * F::D];       // 2^(G_T - Ca) (second half: discarded writes)
 };
 
-// Loads N consecutive bf16 as floats (N in {4, 8, 16}); p is 8- or 16-byte aligned.
+// Loads N consecutive bf16 (N in {4, 8, 16}) as packed words.
 template <int N>
-__device__ __forceinline__ void load_bf16(const u16* p, float* out) {
+__device__ __forceinline__ void load_words(const u16* p, unsigned* w) {
   if constexpr (N == 4) {
-    u32x2_t w = *reinterpret_cast<const u32x2_t*>(p);
-    out[0] = bflo(w[0]); out[1] = bfhi(w[0]); out[2] = bflo(w[1]); out[3] = bfhi(w[1]);
+    u32x2_t x = *reinterpret_cast<const u32x2_t*>(p);
+    w[0] = x[0]; w[1] = x[1];
   } else {
 #pragma unroll
     for (int h = 0; h < N / 8; ++h) {
-      u32x4_t w = *reinterpret_cast<const u32x4_t*>(p + 8 * h);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        out[8 * h + 2 * e] = bflo(w[e]);
-        out[8 * h + 2 * e + 1] = bfhi(w[e]);
-      }
+      u32x4_t x = *reinterpret_cast<const u32x4_t*>(p + 8 * h);
+      w[4 * h] = x[0]; w[4 * h + 1] = x[1]; w[4 * h + 2] = x[2]; w[4 * h + 3] = x[3];
     }
   }
 }
-
-// Stores N floats as bf16 to LDS (N in {4, 8, 16}).
 template <int N>
-__device__ __forceinline__ void store_bf16(u16* p, const float* x) {
+__device__ __forceinline__ void store_words(u16* p, const unsigned* w) {
   if constexpr (N == 4) {
-    u32x2_t w = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
-    *reinterpret_cast<u32x2_t*>(p) = w;
+    *reinterpret_cast<u32x2_t*>(p) = u32x2_t{w[0], w[1]};
   } else {
 #pragma unroll
-    for (int h = 0; h < N / 8; ++h) {
-      u32x4_t w = {pack_bf16(x[8 * h], x[8 * h + 1]), pack_bf16(x[8 * h + 2], x[8 * h + 3]),
-                   pack_bf16(x[8 * h + 4], x[8 * h + 5]), pack_bf16(x[8 * h + 6], x[8 * h + 7])};
-      *reinterpret_cast<u32x4_t*>(p + 8 * h) = w;
-    }
+    for (int h = 0; h < N / 8; ++h)
+      *reinterpret_cast<u32x4_t*>(p + 8 * h) =
+          u32x4_t{w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]};
   }
+}
+// Stores N floats as bf16 (N in {4, 8, 16}).
+template <int N>
+__device__ __forceinline__ void store_bf16(u16* p, const float* x) {
+  unsigned w[N / 2];
+#pragma unroll
+  for (int e = 0; e < N / 2; ++e) w[e] = pack_bf16(x[2 * e], x[2 * e + 1]);
+  store_words<N>(p, w);
 }
 
 // A operand (16 rows x 32 reductions) of a 16x16x32 MFMA read from a bf16 row-major
@@ -165,27 +203,96 @@ __device__ __forceinline__ void store_bf16(u16* p, const float* x) {
 __device__ __forceinline__ u32x4_t lds_a_pi(const u16* row, int k0, int g) {
   u32x2_t lo = *reinterpret_cast<const u32x2_t*>(row + k0 + 4 * g);
   u32x2_t hi = *reinterpret_cast<const u32x2_t*>(row + k0 + 16 + 4 * g);
-  u32x4_t r = {lo[0], lo[1], hi[0], hi[1]};
-  return r;
-}
-
-// Two accumulator tiles (rows 4g+i and 16+4g+i of one 32-row block) -> bf16 B operand.
-__device__ __forceinline__ u32x4_t acc_pair_to_b(f32x4_t t0, f32x4_t t1) {
-  u32x4_t r = {pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]), pack_bf16(t1[0], t1[1]),
-               pack_bf16(t1[2], t1[3])};
-  return r;
-}
-// One accumulator tile (rows 4g+i of a 16-row block) -> bf16 B operand whose
-// reduction slots 4-7 are zero.
-__device__ __forceinline__ u32x4_t acc_to_b_pad(f32x4_t t0) {
-  u32x4_t r = {pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]), 0u, 0u};
-  return r;
+  return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
 }
 // A operand for a 16-long reduction: row r, columns 4g .. 4g+3, slots 4-7 zero.
 __device__ __forceinline__ u32x4_t lds_a_pad(const u16* row, int g) {
   u32x2_t lo = *reinterpret_cast<const u32x2_t*>(row + 4 * g);
-  u32x4_t r = {lo[0], lo[1], 0u, 0u};
-  return r;
+  return u32x4_t{lo[0], lo[1], 0u, 0u};
+}
+// Transposed A operand from a bf16 row-major [C][ld] tile: MFMA row m = key column
+// k0 + m, reduction slots = chunk rows (pi_g: 4g+i, then 16+4g+i).  Built from LDS
+// transpose reads: inside each 16-lane group, lane i of the result takes element
+// i%4 of the 4-element pieces addressed by lanes i/4, 4+i/4, 8+i/4 and 12+i/4, so
+// lane j addresses row 4g + j/4, columns k0 + 4(j%4) .. +3.
+__device__ __forceinline__ s16x4_t ds_read_tr(const u16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(p));
+}
+template <int LD, bool TWO>
+__device__ __forceinline__ u32x4_t lds_a_tr(const u16* tile, int k0, int l16, int g) {
+  const u16* p = tile + (4 * g + (l16 >> 2)) * LD + k0 + 4 * (l16 & 3);
+  const u32x2_t lo = __builtin_bit_cast(u32x2_t, ds_read_tr(p));
+  if constexpr (TWO) {
+    const u32x2_t hi = __builtin_bit_cast(u32x2_t, ds_read_tr(p + 16 * LD));
+    return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  } else {
+    return u32x4_t{lo[0], lo[1], 0u, 0u};
+  }
+}
+
+// Two accumulator tiles (rows 4g+i and 16+4g+i of one 32-row block) -> bf16 B operand.
+__device__ __forceinline__ u32x4_t acc_pair_to_b(f32x4_t t0, f32x4_t t1) {
+  return u32x4_t{pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]), pack_bf16(t1[0], t1[1]),
+                 pack_bf16(t1[2], t1[3])};
+}
+// One accumulator tile (rows 4g+i of a 16-row block) -> bf16 B operand, slots 4-7 zero.
+__device__ __forceinline__ u32x4_t acc_to_b_pad(f32x4_t t0) {
+  return u32x4_t{pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]), 0u, 0u};
+}
+
+// Sum over aligned groups of G lanes (G in {2, 4, 8, 16, 32}) with DPP inside 16-lane rows:
+// quad_perm xor 1, xor 2, then row_half_mirror (pairs quads) and row_mirror (pairs halves).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf,
+                                                            0xf, false));
+}
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(G == 2 || G == 4 || G == 8 || G == 16 || G == 32, "group size");
+  v += dpp_f<0xB1>(v);                       // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) v += dpp_f<0x4E>(v);  // quad_perm [2,3,0,1]
+  if constexpr (G >= 8) v += dpp_f<0x141>(v); // row_half_mirror
+  if constexpr (G >= 16) v += dpp_f<0x140>(v); // row_mirror
+  if constexpr (G >= 32) v += __shfl_xor(v, 16, 64);  // across the two rows
+  return v;
+}
+
+// Broadcast quad lane k's value to the four lanes of every quad (DPP quad_perm).
+template <int K>
+__device__ __forceinline__ float quad_bcast_k(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), K * 0x55,
+                                                            0xf, 0xf, false));
+}
+__device__ __forceinline__ float quad_bcast(float v, int k) {
+  switch (k) {
+    case 0: return quad_bcast_k<0>(v);
+    case 1: return quad_bcast_k<1>(v);
+    case 2: return quad_bcast_k<2>(v);
+    default: return quad_bcast_k<3>(v);
+  }
+}
+
+// Raw buffer descriptor over [base, base + bytes): loads past the end return zero
+// and stores past it are dropped (third word: the gfx9 raw-buffer format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// Loads N consecutive bf16 (N in {4, 8, 16}) as packed words through a descriptor.
+template <int N>
+__device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, unsigned* w) {
+  if constexpr (N == 4) {
+    const u32x2_t x = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    w[0] = x[0]; w[1] = x[1];
+  } else {
+#pragma unroll
+    for (int hh = 0; hh < N / 8; ++hh) {
+      const u32x4_t x =
+          __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * hh, 0, 0));
+      w[4 * hh] = x[0]; w[4 * hh + 1] = x[1]; w[4 * hh + 2] = x[2]; w[4 * hh + 3] = x[3];
+    }
+  }
 }
 
 template <int D, int C, int VT, int NW>
@@ -195,7 +302,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int l16 = lane & 15;
   const int lg = lane >> 4;
 
@@ -215,12 +322,15 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     s1 = s0 + p.T;
   }
   const int64_t H = p.H;
+  const int nchunks = (int)((s1 - s0 + C - 1) / C);
 
   // ---- per-head constants ------------------------------------------------
   const float A = __expf(p.A_log[h]);
-  const int r_row = tid / F::TPR;              // chunk row of the row layout
+  const int r_row = tid / F::TPR;              // chunk row of the row layout (q, k, g)
   const int r_col = (tid % F::TPR) * F::EPT;   // first key column of the row layout
-  float gate_mul = -A * kLog2e;                // sigmoid argument in base 2
+  const int v_row = tid / F::TPRV;             // chunk row of the value row layout
+  const int v_col = (tid % F::TPRV) * F::EPV;  // first value column (inside the tile)
+  const float gate_mul = -A * kLog2e;          // sigmoid argument in base 2
   float gate_add[F::EPT];
 #pragma unroll
   for (int e = 0; e < F::EPT; ++e) gate_add[e] = gate_mul * p.dt_bias[(int64_t)h * D + r_col + e];
@@ -236,336 +346,431 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     for (int kt = 0; kt < F::KT; ++kt)
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) {
-        const int vrow = vbase + 16 * nt + l16;
-        const int kcol = 16 * kt + 4 * lg;
-        const int64_t off = sbase + (int64_t)vrow * D + kcol;
-        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+        const int64_t off = sbase + (int64_t)(vbase + 16 * nt + l16) * D + 16 * kt + 4 * lg;
+        f32x4_t sv = {0.f, 0.f, 0.f, 0.f};
         if (p.s_in != nullptr) {
           if (p.s_in_fp32) {
-            s = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.s_in) + off);
+            sv = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.s_in) + off);
           } else {
             u32x2_t w = *reinterpret_cast<const u32x2_t*>(static_cast<const u16*>(p.s_in) + off);
-            s[0] = bflo(w[0]); s[1] = bfhi(w[0]); s[2] = bflo(w[1]); s[3] = bfhi(w[1]);
+            sv[0] = bflo(w[0]); sv[1] = bfhi(w[0]); sv[2] = bflo(w[1]); sv[3] = bfhi(w[1]);
           }
         }
-        S[kt][nt] = s;
+        S[kt][nt] = sv;
       }
   }
 
-  // Zero the fp32 inverse once: blocks above the diagonal are never written.
-  for (int i = tid; i < F::C * F::LDL; i += F::NTHR) (&sm.X[0][0])[i] = 0.f;
-  // Zero the upper 16x16 block of Mqk once (C = 32): it is never written.
+  // Blocks above the diagonal of INV and Mqk are never written: zero them once.
   if constexpr (F::CT == 2) {
-    for (int i = tid; i < 16 * 16; i += F::NTHR) sm.Mqk[i / 16][16 + i % 16] = 0;
+    for (int i = tid; i < 2 * 16 * 16; i += F::NTHR) {
+      const int b = i >> 8, r = (i >> 4) & 15, c = 16 + (i & 15);
+      sm.slot[b].INV[r][c] = 0;
+      sm.slot[b].Mqk[r][c] = 0;
+    }
   }
 
-  for (int64_t c0 = s0; c0 < s1; c0 += C) {
-    const int valid = (s1 - c0) < C ? (int)(s1 - c0) : C;
+  // ---- raw inputs of the next chunk to prepare, in registers ----------------
+  // Buffer loads through a descriptor bounded to the chunk's valid rows: rows past
+  // the end of the sequence read as zero, without branches.  Offsets are 32-bit
+  // (the host bounds C * H * D * 2 below 2^31).
+  const uint32_t row_bytes = (uint32_t)(H * D * 2);
+  const uint32_t off_qkg = (uint32_t)r_row * row_bytes + (uint32_t)r_col * 2;
+  const uint32_t off_v = (uint32_t)v_row * row_bytes + (uint32_t)(vt_idx * VT + v_col) * 2;
+  const uint32_t off_b = (uint32_t)tid * (uint32_t)(H * 2);
+  unsigned raw_q[F::EPT / 2], raw_k[F::EPT / 2], raw_g[F::EPT / 2], raw_v[F::EPV / 2];
+  unsigned raw_b = 0;
+  auto chunk_valid = [&](int c) -> int {
+    const int64_t rem = s1 - (s0 + (int64_t)c * C);
+    return rem < C ? (int)rem : C;
+  };
+  auto load_raw = [&](int c) {
+    const int64_t cs = s0 + (int64_t)c * C;
+    const int valid = chunk_valid(c);
+    const int64_t tok_elem = (cs * H + h) * D;
+    const int nb = valid * (int)row_bytes;
+    buf_load<F::EPT>(make_rsrc(p.q + tok_elem, nb), off_qkg, raw_q);
+    buf_load<F::EPT>(make_rsrc(p.k + tok_elem, nb), off_qkg, raw_k);
+    buf_load<F::EPT>(make_rsrc(p.g + tok_elem, nb), off_qkg, raw_g);
+    buf_load<F::EPV>(make_rsrc(p.v + tok_elem, nb), off_v, raw_v);
+    raw_b = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(p.beta + cs * H + h, valid * (int)H * 2),
+                                                 off_b, 0, 0);
+  };
 
-    // ---- 1. loads, norms, gate (row layout) ------------------------------
-    float qv[F::EPT], kv[F::EPT];
-    {
-      const bool rv = r_row < valid;
-      float gv[F::EPT];
-      if (rv) {
-        const int64_t off = ((c0 + r_row) * H + h) * D + r_col;
-        load_bf16<F::EPT>(p.q + off, qv);
-        load_bf16<F::EPT>(p.k + off, kv);
-        load_bf16<F::EPT>(p.g + off, gv);
-      } else {
-#pragma unroll
-        for (int e = 0; e < F::EPT; ++e) { qv[e] = 0.f; kv[e] = 0.f; gv[e] = 0.f; }
-      }
-      float sq = 0.f, sk = 0.f;
-#pragma unroll
-      for (int e = 0; e < F::EPT; ++e) {
-        sq = __builtin_fmaf(qv[e], qv[e], sq);
-        sk = __builtin_fmaf(kv[e], kv[e], sk);
-      }
-#pragma unroll
-      for (int m = 1; m < F::TPR; m <<= 1) {
-        sq += __shfl_xor(sq, m, 64);
-        sk += __shfl_xor(sk, m, 64);
-      }
-      const float rq = p.scale * __builtin_amdgcn_rsqf(sq + kNormEps);
-      const float rk = __builtin_amdgcn_rsqf(sk + kNormEps);
-      float lam[F::EPT];
-#pragma unroll
-      for (int e = 0; e < F::EPT; ++e) {
-        qv[e] *= rq;
-        kv[e] *= rk;
-        const float sg = __builtin_amdgcn_rcpf(
-            1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(gv[e], gate_mul, gate_add[e])));
-        lam[e] = rv ? p.lb2 * sg : 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < F::EPT; e += 4) {
-        f32x4_t w = {lam[e], lam[e + 1], lam[e + 2], lam[e + 3]};
-        *reinterpret_cast<f32x4_t*>(&sm.G[r_row][r_col + e]) = w;
-      }
-    }
-    // value tile (16-byte pieces)
-    for (int pc = tid; pc < C * VT / 8; pc += F::NTHR) {
-      const int row = pc / (VT / 8);
-      const int col = (pc % (VT / 8)) * 8;
-      u32x4_t w = {0u, 0u, 0u, 0u};
-      if (row < valid)
-        w = *reinterpret_cast<const u32x4_t*>(p.v + ((c0 + row) * H + h) * D + vt_idx * VT + col);
-      *reinterpret_cast<u32x4_t*>(&sm.V[row][col]) = w;
-    }
-    if (tid < C) sm.beta[tid] = tid < valid ? fast_sigmoid(bf2f(p.beta[(c0 + tid) * H + h])) : 0.f;
-    __syncthreads();
+  // normalised q, k of the chunk being prepared (row layout), phase A -> phase C
+  float qn[F::EPT], kn[F::EPT];
+  f32x4_t P[F::CT][F::NTW], O[F::CT][F::NTW];
 
-    // ---- 2. inclusive prefix over the chunk (column layout) ----------------
-    {
-      const int col = tid % D;
-      const int grp = tid / D;
-      float run[F::RPG];
-      float acc = 0.f;
+  // ======================= phase bodies ======================================
+  // A (prep): gate, norms, value tile and beta of the next chunk.
+  auto prep_A = [&](Slot<F>& nxt, int nxt_valid) {
+    const float lbv = r_row < nxt_valid ? p.lb2 : 0.f;  // rows past the sequence: no decay
+    float gv[F::EPT];
 #pragma unroll
-      for (int i = 0; i < F::RPG; ++i) {
-        acc += sm.G[grp * F::RPG + i][col];
-        run[i] = acc;
-      }
-      sm.tot[grp][col] = acc;
-      __syncthreads();
-      float off = 0.f;
-#pragma unroll
-      for (int gg = 0; gg < F::NGRP - 1; ++gg)
-        if (gg < grp) off += sm.tot[gg][col];
-#pragma unroll
-      for (int i = 0; i < F::RPG; ++i) sm.G[grp * F::RPG + i][col] = run[i] + off;
-      if (grp == F::NGRP - 1) {
-        const float gt = acc + off;
-        sm.a[col] = __builtin_amdgcn_exp2f(gt);
-        sm.gtc[col] = __builtin_amdgcn_exp2f(gt - Ca);
-      }
+    for (int e = 0; e < F::EPT / 2; ++e) {
+      qn[2 * e] = bflo(raw_q[e]); qn[2 * e + 1] = bfhi(raw_q[e]);
+      kn[2 * e] = bflo(raw_k[e]); kn[2 * e + 1] = bfhi(raw_k[e]);
+      gv[2 * e] = bflo(raw_g[e]); gv[2 * e + 1] = bfhi(raw_g[e]);
     }
-    __syncthreads();
-
-    // ---- 3. exponent-scaled operands (row layout) ---------------------------
-    {
-      float oQc[F::EPT], oKc[F::EPT], oKi[F::EPT], oQd[F::EPT], oKd[F::EPT];
+    float sq = 0.f, sk = 0.f;
 #pragma unroll
-      for (int e = 0; e < F::EPT; ++e) {
-        const float d = sm.G[r_row][r_col + e] - Ca;
-        const float e1 = __builtin_amdgcn_exp2f(d);   // 2^(G - Ca)
-        const float e2 = __builtin_amdgcn_exp2f(-d);  // 2^(Ca - G)
-        const float ed = e1 * c1;                     // 2^G
-        oQc[e] = qv[e] * e1;
-        oKc[e] = kv[e] * e1;
-        oKi[e] = kv[e] * e2;
-        oQd[e] = qv[e] * ed;
-        oKd[e] = kv[e] * ed;
-        sm.KrT[r_col + e][r_row] = to_bf16(oKi[e] * sm.gtc[r_col + e]);  // kh 2^(G_T - G)
-      }
-      store_bf16<F::EPT>(&sm.Qc[r_row][r_col], oQc);
-      store_bf16<F::EPT>(&sm.Kc[r_row][r_col], oKc);
-      store_bf16<F::EPT>(&sm.Ki[r_row][r_col], oKi);
-      store_bf16<F::EPT>(&sm.Qd[r_row][r_col], oQd);
-      store_bf16<F::EPT>(&sm.Kd[r_row][r_col], oKd);
+    for (int e = 0; e < F::EPT; ++e) {
+      sq = __builtin_fmaf(qn[e], qn[e], sq);
+      sk = __builtin_fmaf(kn[e], kn[e], sk);
     }
-    __syncthreads();
-
-    // ---- 4. intra-chunk products: L and Mqk (bf16 MFMA) ---------------------
-    {
-      constexpr int NTRI = F::CT * (F::CT + 1) / 2;
-      for (int job = wave; job < 2 * NTRI; job += NW) {
-        const int which = job / NTRI;  // 0: L, 1: Mqk
-        const int tri = job % NTRI;
-        const int ti = tri == 0 ? 0 : (tri == 1 ? 1 : 1);
-        const int tj = tri == 0 ? 0 : (tri == 1 ? 0 : 1);
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        const u16* arow = which ? &sm.Qc[16 * ti + l16][0] : &sm.Kc[16 * ti + l16][0];
-        const u16* brow = &sm.Ki[16 * tj + l16][0];
+    sq = group_sum<F::TPR>(sq);
+    sk = group_sum<F::TPR>(sk);
+    const float rq = p.scale * __builtin_amdgcn_rsqf(sq + kNormEps);
+    const float rk = __builtin_amdgcn_rsqf(sk + kNormEps);
+    float lam[F::EPT];
 #pragma unroll
-        for (int s = 0; s < F::KS; ++s) {
-          u32x4_t a = *reinterpret_cast<const u32x4_t*>(arow + 32 * s + 8 * lg);
-          u32x4_t b = *reinterpret_cast<const u32x4_t*>(brow + 32 * s + 8 * lg);
-          acc = mfma_k32(a, b, acc);
-        }
-        const int j = 16 * tj + l16;
+    for (int e = 0; e < F::EPT; ++e) {
+      qn[e] *= rq;
+      kn[e] *= rk;
+      const float sg = __builtin_amdgcn_rcpf(
+          1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(gv[e], gate_mul, gate_add[e])));
+      lam[e] = lbv * sg;
+    }
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int i = 16 * ti + 4 * lg + ii;
-          if (which == 0) {
-            sm.L[i][j] = (j < i) ? sm.beta[i] * acc[ii] : 0.f;
-          } else {
-            sm.Mqk[i][j] = to_bf16((j <= i) ? acc[ii] : 0.f);
-          }
+    for (int e = 0; e < F::EPT; e += 4)
+      *reinterpret_cast<f32x4_t*>(&sm.G[r_row][r_col + e]) =
+          f32x4_t{lam[e], lam[e + 1], lam[e + 2], lam[e + 3]};
+    store_words<F::EPV>(&nxt.V[v_row][v_col], raw_v);
+    // every thread writes its slot entry; entries past the chunk rows are unused
+    nxt.beta[tid] = tid < nxt_valid ? fast_sigmoid(bf2f((u16)raw_b)) : 0.f;
+  };
+  // A (state): P^T = Kd S^T and O0^T = Qd S^T.
+  auto state_A = [&](Slot<F>& cur) {
+    u32x4_t bS[F::KS][F::NTW];
+#pragma unroll
+    for (int ks = 0; ks < F::KS; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < F::NTW; ++nt)
+        bS[ks][nt] = acc_pair_to_b(S[2 * ks][nt], S[2 * ks + 1][nt]);
+#pragma unroll
+    for (int ct = 0; ct < F::CT; ++ct)
+#pragma unroll
+      for (int nt = 0; nt < F::NTW; ++nt) {
+        P[ct][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        O[ct][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int ct = 0; ct < F::CT; ++ct)
+#pragma unroll
+      for (int ks = 0; ks < F::KS; ++ks) {
+        const u32x4_t aK = lds_a_pi(&cur.Kd[16 * ct + l16][0], 32 * ks, lg);
+        const u32x4_t aQ = lds_a_pi(&cur.Qd[16 * ct + l16][0], 32 * ks, lg);
+#pragma unroll
+        for (int nt = 0; nt < F::NTW; ++nt) {
+          P[ct][nt] = mfma_k32(aK, bS[ks][nt], P[ct][nt]);
+          O[ct][nt] = mfma_k32(aQ, bS[ks][nt], O[ct][nt]);
         }
       }
-    }
-    __syncthreads();
-
-    // ---- 5. INV = (I + L)^-1 (fp32) ------------------------------------------
-    if (wave == 0) {
-      // diagonal 16x16 blocks by forward substitution: lane m of block b owns
-      // column m of that block; x_i = [i == m] - sum_{j < i} L_ij x_j inside it.
-      const int m = lane & 15;
-      const int base = (F::CT == 2) ? 16 * ((lane >> 4) & 1) : 0;
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = (i == m) ? 1.f : 0.f;
-#pragma unroll
-        for (int j = 0; j < i; ++j) s = __builtin_fmaf(-sm.L[base + i][base + j], x[j], s);
-        x[i] = s;
-      }
-      if (lane < C) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sm.X[base + i][base + m] = x[i];
-      }
-    }
-    __syncthreads();
+  };
+  // A (wave 0): X21 = -X22 (L21 X11) of the current chunk on the fp32 MFMA; lane l
+  // supplies A[l&15][k] and B[k][l&15] with k = 4 q + (l >> 4).
+  auto inv_offdiag = [&](Slot<F>& cur) {
     if constexpr (F::CT == 2) {
-      // X21 = -X22 (L21 X11) on the fp32 MFMA: lane l supplies A[l&15][k] and
-      // B[k][l&15] with k = 4s + (l >> 4); results come back in accumulator layout.
       if (wave == 0) {
         f32x4_t y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int kk = 4 * s + lg;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int kk = 4 * q4 + lg;
           y = mfma_f32(sm.L[16 + l16][kk], sm.X[kk][l16], y);
         }
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) sm.Y[4 * lg + ii][l16] = y[ii];
-      }
-      __syncthreads();
-      if (wave == 0) {
+        wave_lds_sync();
         f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int kk = 4 * s + lg;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int kk = 4 * q4 + lg;
           z = mfma_f32(sm.X[16 + l16][16 + kk], sm.Y[kk][l16], z);
         }
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) sm.X[16 + 4 * lg + ii][l16] = -z[ii];
+        for (int ii = 0; ii < 4; ++ii) cur.INV[16 + 4 * lg + ii][l16] = to_bf16(-z[ii]);
       }
-      __syncthreads();
     }
-    for (int i = tid; i < C * C; i += F::NTHR) sm.INV[i / C][i % C] = to_bf16(sm.X[i / C][i % C]);
-    __syncthreads();
-
-    // ---- 6. state side (each wave: its value columns) -----------------------
-    {
-      // B operands from the bf16 copy of S^T
-      u32x4_t bS[F::KS][F::NTW];
+  };
+  // B (prep): inclusive prefix over the chunk rows.  Each wave scans SCOLS columns
+  // as 16 columns x 4 row groups; group offsets are combined across lanes.
+  auto prep_B = [&](Slot<F>& nxt) {
 #pragma unroll
-      for (int s = 0; s < F::KS; ++s)
+    for (int ps = 0; ps < F::SPASS; ++ps) {
+      const int col = wave * F::SCOLS + 16 * ps + l16;
+      const int r0 = lg * F::RPG;
+      float run[F::RPG];
+      float acc = 0.f;
 #pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt) bS[s][nt] = acc_pair_to_b(S[2 * s][nt], S[2 * s + 1][nt]);
-
-      f32x4_t P[F::CT][F::NTW], O[F::CT][F::NTW];
+      for (int i = 0; i < F::RPG; ++i) {
+        acc += sm.G[r0 + i][col];
+        run[i] = acc;
+      }
+      // Exclusive prefix of the four group totals r0..r3 (one per 16-lane row) with
+      // the lane-swap instructions: the 16-row swap gives [r0, r0, r2, r2] and
+      // [r1, r1, r3, r3]; their sum swapped across the 32-lane halves gives r0 + r1
+      // to rows 2 and 3.
+      const unsigned ab = __builtin_bit_cast(unsigned, acc);
+      const auto sw16 = __builtin_amdgcn_permlane16_swap(ab, ab, false, false);
+      const float below = __builtin_bit_cast(float, (unsigned)sw16[0]);  // row g-1 for odd g
+      const float pair = below + __builtin_bit_cast(float, (unsigned)sw16[1]);
+      const unsigned pb = __builtin_bit_cast(unsigned, pair);
+      const auto sw32 = __builtin_amdgcn_permlane32_swap(pb, pb, false, false);
+      const float lower = __builtin_bit_cast(float, (unsigned)sw32[0]);  // r0 + r1
+      const float off = ((lg & 1) ? below : 0.f) + (lg >= 2 ? lower : 0.f);
 #pragma unroll
-      for (int ct = 0; ct < F::CT; ++ct)
+      for (int i = 0; i < F::RPG; ++i) sm.G[r0 + i][col] = run[i] + off;
+      // G_T is the last row, held by lane group 3; the other groups write the
+      // same expressions into a discarded half of each array (no branch).
+      const float gt = run[F::RPG - 1] + off;
+      const int dst = (lg == 3) ? col : F::D + col;
+      nxt.a[dst] = __builtin_amdgcn_exp2f(gt);
+      sm.gtc[dst] = __builtin_amdgcn_exp2f(gt - Ca);
+    }
+  };
+  // B (state): R, U, the state update and the output of the current chunk.
+  auto state_B = [&](Slot<F>& cur) {
+    // R^T = diag(beta) (V - P^T), in place in P
 #pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt) {
-          P[ct][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          O[ct][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < F::CT; ++ct) {
+      const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(&cur.beta[16 * ct + 4 * lg]);
+#pragma unroll
+      for (int nt = 0; nt < F::NTW; ++nt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int c = 16 * ct + 4 * lg + ii;
+          const int vc = wave * 16 * F::NTW + 16 * nt + l16;
+          P[ct][nt][ii] = b4[ii] * (bf2f(cur.V[c][vc]) - P[ct][nt][ii]);
         }
+    }
+    f32x4_t U[F::CT][F::NTW];
+    if constexpr (F::CT == 2) {
+      u32x4_t bR[F::NTW];
 #pragma unroll
-      for (int ct = 0; ct < F::CT; ++ct)
+      for (int nt = 0; nt < F::NTW; ++nt) bR[nt] = acc_pair_to_b(P[0][nt], P[1][nt]);
 #pragma unroll
-        for (int s = 0; s < F::KS; ++s) {
-          const u32x4_t aK = lds_a_pi(&sm.Kd[16 * ct + l16][0], 32 * s, lg);
-          const u32x4_t aQ = lds_a_pi(&sm.Qd[16 * ct + l16][0], 32 * s, lg);
-#pragma unroll
-          for (int nt = 0; nt < F::NTW; ++nt) {
-            P[ct][nt] = mfma_k32(aK, bS[s][nt], P[ct][nt]);
-            O[ct][nt] = mfma_k32(aQ, bS[s][nt], O[ct][nt]);
-          }
-        }
-
-      // R^T = diag(beta) (V - P^T), in place in P
-#pragma unroll
-      for (int ct = 0; ct < F::CT; ++ct)
+      for (int ct = 0; ct < 2; ++ct) {
+        const u32x4_t aI = lds_a_pi(&cur.INV[16 * ct + l16][0], 0, lg);
 #pragma unroll
         for (int nt = 0; nt < F::NTW; ++nt)
+          U[ct][nt] = mfma_k32(aI, bR[nt], f32x4_t{0.f, 0.f, 0.f, 0.f});
+      }
+      u32x4_t bU[F::NTW];
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const int c = 16 * ct + 4 * lg + ii;
-            const int vc = wave * 16 * F::NTW + 16 * nt + l16;
-            P[ct][nt][ii] = sm.beta[c] * (bf2f(sm.V[c][vc]) - P[ct][nt][ii]);
-          }
-
-      // U^T = INV R^T, then the bf16 B operands of U^T
-      f32x4_t U[F::CT][F::NTW];
-      if constexpr (F::CT == 2) {
-        u32x4_t bR[F::NTW];
+      for (int nt = 0; nt < F::NTW; ++nt) bU[nt] = acc_pair_to_b(U[0][nt], U[1][nt]);
 #pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt) bR[nt] = acc_pair_to_b(P[0][nt], P[1][nt]);
+      for (int kt = 0; kt < F::KT; ++kt) {
+        const f32x4_t av = *reinterpret_cast<const f32x4_t*>(&cur.a[16 * kt + 4 * lg]);
+        const u32x4_t aR = lds_a_tr<F::LDR, true>(&cur.Kr[0][0], 16 * kt, l16, lg);
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const u32x4_t aI = lds_a_pi(&sm.INV[16 * ct + l16][0], 0, lg);
+        for (int nt = 0; nt < F::NTW; ++nt) S[kt][nt] = mfma_k32(aR, bU[nt], S[kt][nt] * av);
+      }
 #pragma unroll
-          for (int nt = 0; nt < F::NTW; ++nt)
-            U[ct][nt] = mfma_k32(aI, bR[nt], f32x4_t{0.f, 0.f, 0.f, 0.f});
-        }
-        u32x4_t bU[F::NTW];
+      for (int ct = 0; ct < 2; ++ct) {
+        const u32x4_t aM = lds_a_pi(&cur.Mqk[16 * ct + l16][0], 0, lg);
 #pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt) bU[nt] = acc_pair_to_b(U[0][nt], U[1][nt]);
-        // S^T <- diag(a) S^T + Kr^T U^T
+        for (int nt = 0; nt < F::NTW; ++nt) O[ct][nt] = mfma_k32(aM, bU[nt], O[ct][nt]);
+      }
+    } else {
+      // 16-token chunks: the same 16x16x32 instruction with reduction slots 4-7
+      // zero in both operands (one MFMA shape on every accumulator chain).
+      u32x4_t bR[F::NTW];
 #pragma unroll
-        for (int kt = 0; kt < F::KT; ++kt) {
-          f32x4_t av = *reinterpret_cast<const f32x4_t*>(&sm.a[16 * kt + 4 * lg]);
-          const u32x4_t aR = lds_a_pi(&sm.KrT[16 * kt + l16][0], 0, lg);
+      for (int nt = 0; nt < F::NTW; ++nt) bR[nt] = acc_to_b_pad(P[0][nt]);
+      const u32x4_t aI = lds_a_pad(&cur.INV[l16][0], lg);
 #pragma unroll
-          for (int nt = 0; nt < F::NTW; ++nt) {
-            S[kt][nt] = S[kt][nt] * av;
-            S[kt][nt] = mfma_k32(aR, bU[nt], S[kt][nt]);
-          }
-        }
-        // O^T = O0^T + Mqk U^T
+      for (int nt = 0; nt < F::NTW; ++nt)
+        U[0][nt] = mfma_k32(aI, bR[nt], f32x4_t{0.f, 0.f, 0.f, 0.f});
+      u32x4_t bU[F::NTW];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const u32x4_t aM = lds_a_pi(&sm.Mqk[16 * ct + l16][0], 0, lg);
+      for (int nt = 0; nt < F::NTW; ++nt) bU[nt] = acc_to_b_pad(U[0][nt]);
 #pragma unroll
-          for (int nt = 0; nt < F::NTW; ++nt) O[ct][nt] = mfma_k32(aM, bU[nt], O[ct][nt]);
+      for (int kt = 0; kt < F::KT; ++kt) {
+        const f32x4_t av = *reinterpret_cast<const f32x4_t*>(&cur.a[16 * kt + 4 * lg]);
+        const u32x4_t aR = lds_a_tr<F::LDR, false>(&cur.Kr[0][0], 16 * kt, l16, lg);
+#pragma unroll
+        for (int nt = 0; nt < F::NTW; ++nt) S[kt][nt] = mfma_k32(aR, bU[nt], S[kt][nt] * av);
+      }
+      const u32x4_t aM = lds_a_pad(&cur.Mqk[l16][0], lg);
+#pragma unroll
+      for (int nt = 0; nt < F::NTW; ++nt) O[0][nt] = mfma_k32(aM, bU[nt], O[0][nt]);
+    }
+    // stage O^T as bf16 [token][value] for coalesced stores
+#pragma unroll
+    for (int ct = 0; ct < F::CT; ++ct)
+#pragma unroll
+      for (int nt = 0; nt < F::NTW; ++nt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          sm.Ost[16 * ct + 4 * lg + ii][wave * 16 * F::NTW + 16 * nt + l16] =
+              to_bf16(O[ct][nt][ii]);
+  };
+  // C (prep): exponent-scaled operands of the next chunk.
+  auto prep_C = [&](Slot<F>& nxt) {
+    float oQc[F::EPT], oKc[F::EPT], oKi[F::EPT], oQd[F::EPT], oKd[F::EPT], oKr[F::EPT];
+    float gv[F::EPT], gt[F::EPT];
+#pragma unroll
+    for (int e = 0; e < F::EPT; e += 4) {
+      const f32x4_t gg = *reinterpret_cast<const f32x4_t*>(&sm.G[r_row][r_col + e]);
+      const f32x4_t tt = *reinterpret_cast<const f32x4_t*>(&sm.gtc[r_col + e]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { gv[e + j] = gg[j]; gt[e + j] = tt[j]; }
+    }
+#pragma unroll
+    for (int e = 0; e < F::EPT; ++e) {
+      const float d = gv[e] - Ca;
+      const float e1 = __builtin_amdgcn_exp2f(d);   // 2^(G - Ca)
+      const float e2 = __builtin_amdgcn_exp2f(-d);  // 2^(Ca - G)
+      const float ed = e1 * c1;                     // 2^G
+      oQc[e] = qn[e] * e1;
+      oKc[e] = kn[e] * e1;
+      oKi[e] = kn[e] * e2;
+      oQd[e] = qn[e] * ed;
+      oKd[e] = kn[e] * ed;
+      oKr[e] = oKi[e] * gt[e];                      // kh 2^(G_T - G)
+    }
+    store_bf16<F::EPT>(&sm.Qc[r_row][r_col], oQc);
+    store_bf16<F::EPT>(&sm.Kc[r_row][r_col], oKc);
+    store_bf16<F::EPT>(&sm.Ki[r_row][r_col], oKi);
+    store_bf16<F::EPT>(&nxt.Qd[r_row][r_col], oQd);
+    store_bf16<F::EPT>(&nxt.Kd[r_row][r_col], oKd);
+    store_bf16<F::EPT>(&nxt.Kr[r_row][r_col], oKr);
+  };
+  // C (state): the staged output of the current chunk, 16 bytes per store; the
+  // descriptor covers the valid rows only, so stores past the sequence are dropped.
+  auto store_out = [&](int64_t cur_start, int cur_valid) {
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(p.out + (cur_start * H + h) * D + vt_idx * VT, cur_valid * (int)row_bytes);
+    constexpr int NPC = C * VT / 8;
+#pragma unroll
+    for (int it = 0; it < (NPC + F::NTHR - 1) / F::NTHR; ++it) {
+      const int pc = tid + it * F::NTHR;
+      if constexpr (NPC % F::NTHR != 0) {
+        if (pc >= NPC) break;
+      }
+      const int row = pc / (VT / 8);
+      const int col = (pc % (VT / 8)) * 8;
+      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(&sm.Ost[row][col]);
+      __builtin_amdgcn_raw_buffer_store_b128(w, ro, (uint32_t)row * row_bytes + (uint32_t)col * 2,
+                                             0, 0);
+    }
+  };
+  // D (prep): intra-chunk products and the diagonal inverse blocks.  Job j runs
+  // on wave j % NW; jobs 0..NTRI-1 are L tiles, the rest Mqk tiles; the wave of
+  // each diagonal L tile then inverts that block.
+  auto prep_D = [&](Slot<F>& nxt) {
+    constexpr int NTRI = F::CT * (F::CT + 1) / 2;
+    for (int job = wave; job < 2 * NTRI; job += NW) {
+      const int which = job / NTRI;  // 0: L, 1: Mqk
+      const int tri = job % NTRI;
+      const int ti = tri == 0 ? 0 : 1;
+      const int tj = tri == 2 ? 1 : 0;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      const u16* arow = which ? &sm.Qc[16 * ti + l16][0] : &sm.Kc[16 * ti + l16][0];
+      const u16* brow = &sm.Ki[16 * tj + l16][0];
+#pragma unroll
+      for (int ks = 0; ks < F::KS; ++ks) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(arow + 32 * ks + 8 * lg);
+        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(brow + 32 * ks + 8 * lg);
+        acc = mfma_k32(a, b, acc);
+      }
+      const int j = 16 * tj + l16;
+      if (which == 0) {
+        const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(&nxt.beta[16 * ti + 4 * lg]);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int i = 16 * ti + 4 * lg + ii;
+          sm.L[i][j] = (j < i) ? b4[ii] * acc[ii] : 0.f;
         }
       } else {
-        // 16-token chunks: the same 16x16x32 instruction with reduction slots 4-7
-        // zero in both operands (one MFMA shape on every accumulator chain).
-        u32x4_t bR[F::NTW];
 #pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt) bR[nt] = acc_to_b_pad(P[0][nt]);
-        const u32x4_t aI = lds_a_pad(&sm.INV[l16][0], lg);
-#pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt)
-          U[0][nt] = mfma_k32(aI, bR[nt], f32x4_t{0.f, 0.f, 0.f, 0.f});
-        u32x4_t bU[F::NTW];
-#pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt) bU[nt] = acc_to_b_pad(U[0][nt]);
-#pragma unroll
-        for (int kt = 0; kt < F::KT; ++kt) {
-          f32x4_t av = *reinterpret_cast<const f32x4_t*>(&sm.a[16 * kt + 4 * lg]);
-          const u32x4_t aR = lds_a_pad(&sm.KrT[16 * kt + l16][0], lg);
-#pragma unroll
-          for (int nt = 0; nt < F::NTW; ++nt) {
-            S[kt][nt] = S[kt][nt] * av;
-            S[kt][nt] = mfma_k32(aR, bU[nt], S[kt][nt]);
-          }
+        for (int ii = 0; ii < 4; ++ii) {
+          const int i = 16 * ti + 4 * lg + ii;
+          nxt.Mqk[i][j] = to_bf16((j <= i) ? acc[ii] : 0.f);
         }
-        const u32x4_t aM = lds_a_pad(&sm.Mqk[l16][0], lg);
-#pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt) O[0][nt] = mfma_k32(aM, bU[nt], O[0][nt]);
       }
-
-      // store O^T -> out[token, h, value] (bf16)
+      if (which == 0 && ti == tj) {
+        // forward substitution of the diagonal block, x_i = [i == m] - sum_{j<i} L_ij x_j
+        // for every column m.  Column m lives in the lane quad 4m..4m+3; quad lane g
+        // owns rows g, g+4, g+8, g+12 and holds those rows of L in registers.  At
+        // step j the finished x_j is broadcast inside each quad (DPP quad_perm) and
+        // every lane updates its four rows; L is zero on and above the diagonal, so
+        // the update needs no masking.
+        wave_lds_sync();
+        const int base = 16 * ti;
+        const int m = lane >> 2;
+        const int gq = lane & 3;
+        float Lr[4][16];
 #pragma unroll
-      for (int ct = 0; ct < F::CT; ++ct)
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt)
+          for (int j4 = 0; j4 < 16; j4 += 4) {
+            const f32x4_t w =
+                *reinterpret_cast<const f32x4_t*>(&sm.L[base + gq + 4 * t][base + j4]);
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const int c = 16 * ct + 4 * lg + ii;
-            if (c < valid) {
-              const int64_t off = ((c0 + c) * H + h) * D + vbase + 16 * nt + l16;
-              p.out[off] = to_bf16(O[ct][nt][ii]);
-            }
+            for (int u = 0; u < 4; ++u) Lr[t][j4 + u] = w[u];
           }
+        float x[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] = (gq + 4 * t == m) ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < 15; ++j) {
+          // x_j sits in quad lane j % 4, register j / 4
+          const float xj = quad_bcast(x[j >> 2], j & 3);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) x[t] = __builtin_fmaf(-Lr[t][j], xj, x[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          sm.X[base + gq + 4 * t][base + m] = x[t];
+          nxt.INV[base + gq + 4 * t][base + m] = to_bf16(x[t]);
+        }
+      }
     }
-    __syncthreads();
+  };
+
+  // ======================= schedule ==========================================
+  if (nchunks > 0) {
+    // prologue: prepare chunk 0 into slot 0
+    load_raw(0);
+    prep_A(sm.slot[0], chunk_valid(0));
+    load_raw(nchunks > 1 ? 1 : 0);
+    lds_barrier();
+    prep_B(sm.slot[0]);
+    lds_barrier();
+    prep_C(sm.slot[0]);
+    lds_barrier();
+    prep_D(sm.slot[0]);
+    lds_barrier();
+    // steady state: state side of chunk s next to the preparation of chunk s+1
+    for (int s = 0; s + 1 < nchunks; ++s) {
+      Slot<F>& cur = sm.slot[s & 1];
+      Slot<F>& nxt = sm.slot[(s + 1) & 1];
+      const int64_t cur_start = s0 + (int64_t)s * C;
+      prep_A(nxt, chunk_valid(s + 1));
+      load_raw(s + 2 < nchunks ? s + 2 : nchunks - 1);
+      state_A(cur);
+      inv_offdiag(cur);
+      lds_barrier();
+      prep_B(nxt);
+      state_B(cur);
+      lds_barrier();
+      prep_C(nxt);
+      store_out(cur_start, C);
+      lds_barrier();
+      prep_D(nxt);
+      lds_barrier();
+    }
+    // epilogue: state side of the last chunk
+    {
+      const int s = nchunks - 1;
+      Slot<F>& cur = sm.slot[s & 1];
+      state_A(cur);
+      inv_offdiag(cur);
+      lds_barrier();
+      state_B(cur);
+      lds_barrier();
+      store_out(s0 + (int64_t)s * C, chunk_valid(s));
+    }
   }
 
   // ---- state out ------------------------------------------------------------
@@ -575,15 +780,13 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     for (int kt = 0; kt < F::KT; ++kt)
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) {
-        const int vrow = vbase + 16 * nt + l16;
-        const int kcol = 16 * kt + 4 * lg;
-        const int64_t off = sbase + (int64_t)vrow * D + kcol;
-        const f32x4_t s = S[kt][nt];
+        const int64_t off = sbase + (int64_t)(vbase + 16 * nt + l16) * D + 16 * kt + 4 * lg;
+        const f32x4_t sv = S[kt][nt];
         if (p.s_out_fp32) {
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.s_out) + off) = s;
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.s_out) + off) = sv;
         } else {
-          u32x2_t w = {pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3])};
-          *reinterpret_cast<u32x2_t*>(static_cast<u16*>(p.s_out) + off) = w;
+          *reinterpret_cast<u32x2_t*>(static_cast<u16*>(p.s_out) + off) =
+              u32x2_t{pack_bf16(sv[0], sv[1]), pack_bf16(sv[2], sv[3])};
         }
       }
   }
@@ -601,8 +804,8 @@ hipError_t launch_one(const KdaParams& p, hipStream_t stream) {
 }  // namespace
 
 #define KDA_SCHEDULES(X)  \
-  X(128, 32, 128, 4)      \
-  X(128, 16, 128, 4)      \
+  X(128, 32, 128, 8)      \
+  X(128, 16, 128, 8)      \
   X(128, 32, 64, 4)       \
   X(128, 16, 64, 4)       \
   X(64, 32, 64, 4)        \
