@@ -15,22 +15,21 @@
 //      with the fixed anchor Ca = (C/2) lb log2(e) (section 2: 16 b for C = 32)
 //   4. L = strictLower(diag(beta) Kc Ki^T), Mqk = lowerTri(Qc Ki^T)  (bf16 MFMA,
 //      masked by select so overflowed upper entries never propagate)
-//   5. INV = (I + L)^-1 in fp32: forward substitution on 16x16 diagonal blocks,
-//      the off-diagonal block by X21 = -X22 L21 X11 on fp32 MFMA
+//   5. (I + L)^-1 in fp32 on the 16x16 diagonal blocks (forward substitution);
+//      the lower-left block is applied as a blocked solve in step 6
 //   6. state side, per wave on its own value columns (section 3):
-//        P^T = Kd S^T, O0^T = Qd S^T, R^T = diag(beta)(V - P^T), U^T = INV R^T,
+//        P^T = Kd S^T, O0^T = Qd S^T, R^T = diag(beta)(V - P^T), U^T = (I+L)^-1 R^T,
 //        S^T <- diag(a) S^T + Kr^T U^T,  O^T = O0^T + Mqk U^T
 //
 // Schedule.  Steps 1-5 only touch chunk-local data, step 6 is the strictly
-// ordered recurrence (section 3's scheduling property).  Step s of the main
-// loop runs the state side of chunk s next to the preparation of chunk s+1,
-// in four phases separated by workgroup barriers that fence LDS only, so the
-// raw inputs of chunk s+2, loaded into registers during step s, stay in flight
-// across them:
-//   A  gate and norms of s+1 (VALU)     | P, O0 of s (MFMA) | X21 of s (wave 0)
-//   B  prefix scan of s+1               | R, U, state update, output of s
-//   C  exponent-scaled operands of s+1  | coalesced store of the output of s
-//   D  L, Mqk and diagonal inverse blocks of s+1
+// ordered recurrence (section 3's scheduling property).  Waves 0..NSW-1 hold the
+// state; the other waves prepare.  Step s of the main loop runs three phases
+// separated by workgroup barriers that fence LDS only, so the raw inputs of
+// chunk s+2, loaded into registers during step s, stay in flight across them:
+//   A  gate and norms of s+1 (all) | P, O0 of s (state waves) |
+//      L, Mqk and the diagonal inverse blocks of s (the other waves)
+//   B  prefix scan of s+1 (all)    | R, blocked solve, state update, output of s
+//   C  exponent-scaled operands of s+1 (all) | coalesced store of the output of s
 // Two LDS slots hold the prepared operands of chunks s and s+1 (the page's
 // prep ring, two deep here).
 //
@@ -103,17 +102,18 @@ __device__ __forceinline__ float fast_sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
 }
 
-template <int D_, int C_, int VT_, int NW_>
+template <int D_, int C_, int VT_, int NW_, int NSW_>
 struct Cfg {
   static constexpr int D = D_;     // key = value head dimension
   static constexpr int C = C_;     // chunk length
   static constexpr int VT = VT_;   // value rows owned by the workgroup
   static constexpr int NW = NW_;   // waves
+  static constexpr int NSW = NSW_; // waves 0..NSW-1 hold the state (and its MFMAs)
   static constexpr int NTHR = NW * 64;
   static constexpr int KT = D / 16;            // 16-row key tiles of S^T
   static constexpr int KS = D / 32;            // 32-wide steps of D-long reductions
   static constexpr int CT = C / 16;            // 16-row chunk tiles
-  static constexpr int NTW = VT / (16 * NW);   // 16-column value tiles per wave
+  static constexpr int NTW = VT / (16 * NSW);  // 16-column value tiles per state wave
   static constexpr int EPT = C * D / NTHR;     // row-layout elements per thread (q, k, g)
   static constexpr int TPR = D / EPT;          // threads per chunk row
   static constexpr int EPV = C * VT / NTHR;    // row-layout elements per thread (v)
@@ -128,13 +128,18 @@ struct Cfg {
   static constexpr int LDV = VT + 8;           // bf16 row stride of [C][VT] value tiles
   static constexpr int LDL = C + 4;            // fp32 row stride of [C][C] tiles
   static_assert(C == 16 || C == 32, "chunk");
-  static_assert(NTW >= 1 && NTW * 16 * NW == VT, "value tiling");
+  static_assert(NSW >= 1 && NSW <= NW, "state waves");
+  static_assert(NTW >= 1 && NTW * 16 * NSW == VT, "value tiling");
   static_assert(EPT == 4 || EPT == 8 || EPT == 16, "row layout");
   static_assert(EPV == 4 || EPV == 8 || EPV == 16, "value row layout");
   static_assert(TPR >= 2 && TPR <= 32, "row reduction: DPP inside rows, one cross-row step");
   static_assert(SPASS >= 1 && SPASS * 16 * NW == D, "scan layout");
   static_assert(D % 32 == 0, "head dim");
   static_assert(NW >= 2, "two waves for the diagonal inverse blocks");
+  // waves that run the chunk-local matrix jobs: four dedicated ones when there
+  // are enough waves beyond the state waves, otherwise every wave takes some
+  static constexpr int JOB_BASE = (NW - NSW >= 4) ? NSW : 0;
+  static constexpr int JOB_STRIDE = (NW - NSW >= 4) ? 4 : NW;
 };
 
 // Prepared operands of one chunk.
@@ -143,7 +148,7 @@ struct alignas(16) Slot {
   u16 Qd[F::C][F::LDQ];
   u16 Kd[F::C][F::LDQ];
   u16 Kr[F::C][F::LDR];
-  u16 INV[F::C][F::LDC];
+  u16 SOL[F::C][F::LDC];     // [[X11, 0], [-L21, X22]]: X = (I + L)^-1 diagonal blocks
   u16 Mqk[F::C][F::LDC];
   u16 V[F::C][F::LDV];
   float a[2 * F::D];         // 2^G_T (second half: discarded writes)
@@ -158,9 +163,7 @@ struct alignas(16) Smem {
   u16 Ki[F::C][F::LDQ];
   u16 Ost[F::C][F::LDV];     // output staging for coalesced stores
   float G[F::C][F::LDG];     // base-2 decay, then its inclusive prefix
-  float L[F::C][F::LDL];     // strictLower(diag(beta) Kc Ki^T)
-  float X[F::C][F::LDL];     // fp32 (I + L)^-1 diagonal blocks
-  float Y[16][17];           // L21 X11 of the blocked inverse
+  float L[F::C][F::LDL];     // diagonal tiles of strictLower(diag(beta) Kc Ki^T)
   float gtc[2 * F::D];       // 2^(G_T - Ca) (second half: discarded writes)
 };
 
@@ -295,9 +298,9 @@ __device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off,
   }
 }
 
-template <int D, int C, int VT, int NW>
+template <int D, int C, int VT, int NW, int NSW>
 __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
-  using F = Cfg<D, C, VT, NW>;
+  using F = Cfg<D, C, VT, NW, NSW>;
   __shared__ Smem<F> sm;
 
   const int tid = threadIdx.x;
@@ -305,6 +308,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int l16 = lane & 15;
   const int lg = lane >> 4;
+  const bool is_state = wave < NSW;  // uniform per wave
 
   // ---- work item ---------------------------------------------------------
   const int vt_idx = blockIdx.x % p.n_vtiles;
@@ -337,34 +341,34 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   const float Ca = p.anchor;
   const float c1 = __builtin_amdgcn_exp2f(Ca);  // 2^Ca
 
-  // ---- state in: S^T accumulators ----------------------------------------
-  const int vbase = vt_idx * VT + wave * 16 * F::NTW;  // first value row of this wave
+  // ---- state in: S^T accumulators of the state waves -------------------------
+  const int vbase = vt_idx * VT + wave * 16 * F::NTW;  // first value row of a state wave
+  const int64_t sbase = ((int64_t)n * H + h) * D * D;
   f32x4_t S[F::KT][F::NTW];
-  {
-    const int64_t sbase = ((int64_t)n * H + h) * D * D;
+#pragma unroll
+  for (int kt = 0; kt < F::KT; ++kt)
+#pragma unroll
+    for (int nt = 0; nt < F::NTW; ++nt) S[kt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (is_state && p.s_in != nullptr) {
 #pragma unroll
     for (int kt = 0; kt < F::KT; ++kt)
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) {
         const int64_t off = sbase + (int64_t)(vbase + 16 * nt + l16) * D + 16 * kt + 4 * lg;
-        f32x4_t sv = {0.f, 0.f, 0.f, 0.f};
-        if (p.s_in != nullptr) {
-          if (p.s_in_fp32) {
-            sv = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.s_in) + off);
-          } else {
-            u32x2_t w = *reinterpret_cast<const u32x2_t*>(static_cast<const u16*>(p.s_in) + off);
-            sv[0] = bflo(w[0]); sv[1] = bfhi(w[0]); sv[2] = bflo(w[1]); sv[3] = bfhi(w[1]);
-          }
+        if (p.s_in_fp32) {
+          S[kt][nt] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.s_in) + off);
+        } else {
+          const u32x2_t w =
+              *reinterpret_cast<const u32x2_t*>(static_cast<const u16*>(p.s_in) + off);
+          S[kt][nt] = f32x4_t{bflo(w[0]), bfhi(w[0]), bflo(w[1]), bfhi(w[1])};
         }
-        S[kt][nt] = sv;
       }
   }
 
-  // Blocks above the diagonal of INV and Mqk are never written: zero them once.
+  // The block above the diagonal of Mqk is never written: zero it once.
   if constexpr (F::CT == 2) {
     for (int i = tid; i < 2 * 16 * 16; i += F::NTHR) {
       const int b = i >> 8, r = (i >> 4) & 15, c = 16 + (i & 15);
-      sm.slot[b].INV[r][c] = 0;
       sm.slot[b].Mqk[r][c] = 0;
     }
   }
@@ -401,7 +405,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   f32x4_t P[F::CT][F::NTW], O[F::CT][F::NTW];
 
   // ======================= phase bodies ======================================
-  // A (prep): gate, norms, value tile and beta of the next chunk.
+  // A (prep, every wave): gate, norms, value tile and beta of the next chunk.
   auto prep_A = [&](Slot<F>& nxt, int nxt_valid) {
     const float lbv = r_row < nxt_valid ? p.lb2 : 0.f;  // rows past the sequence: no decay
     float gv[F::EPT];
@@ -438,14 +442,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     // every thread writes its slot entry; entries past the chunk rows are unused
     nxt.beta[tid] = tid < nxt_valid ? fast_sigmoid(bf2f((u16)raw_b)) : 0.f;
   };
-  // A (state): P^T = Kd S^T and O0^T = Qd S^T.
+  // A (state waves): P^T = Kd S^T and O0^T = Qd S^T.
   auto state_A = [&](Slot<F>& cur) {
-    u32x4_t bS[F::KS][F::NTW];
-#pragma unroll
-    for (int ks = 0; ks < F::KS; ++ks)
-#pragma unroll
-      for (int nt = 0; nt < F::NTW; ++nt)
-        bS[ks][nt] = acc_pair_to_b(S[2 * ks][nt], S[2 * ks + 1][nt]);
 #pragma unroll
     for (int ct = 0; ct < F::CT; ++ct)
 #pragma unroll
@@ -453,41 +451,106 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
         P[ct][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         O[ct][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
+    // one 32-row key step at a time: its bf16 copy of S^T is live only there
 #pragma unroll
-    for (int ct = 0; ct < F::CT; ++ct)
+    for (int ks = 0; ks < F::KS; ++ks) {
+      u32x4_t bS[F::NTW];
 #pragma unroll
-      for (int ks = 0; ks < F::KS; ++ks) {
+      for (int nt = 0; nt < F::NTW; ++nt)
+        bS[nt] = acc_pair_to_b(S[2 * ks][nt], S[2 * ks + 1][nt]);
+#pragma unroll
+      for (int ct = 0; ct < F::CT; ++ct) {
         const u32x4_t aK = lds_a_pi(&cur.Kd[16 * ct + l16][0], 32 * ks, lg);
         const u32x4_t aQ = lds_a_pi(&cur.Qd[16 * ct + l16][0], 32 * ks, lg);
 #pragma unroll
         for (int nt = 0; nt < F::NTW; ++nt) {
-          P[ct][nt] = mfma_k32(aK, bS[ks][nt], P[ct][nt]);
-          O[ct][nt] = mfma_k32(aQ, bS[ks][nt], O[ct][nt]);
+          P[ct][nt] = mfma_k32(aK, bS[nt], P[ct][nt]);
+          O[ct][nt] = mfma_k32(aQ, bS[nt], O[ct][nt]);
         }
       }
+    }
   };
-  // A (wave 0): X21 = -X22 (L21 X11) of the current chunk on the fp32 MFMA; lane l
-  // supplies A[l&15][k] and B[k][l&15] with k = 4 q + (l >> 4).
-  auto inv_offdiag = [&](Slot<F>& cur) {
-    if constexpr (F::CT == 2) {
-      if (wave == 0) {
-        f32x4_t y = {0.f, 0.f, 0.f, 0.f};
+  // A (job waves): the chunk-local matrices of the current chunk from its centred
+  // operands.  One 16x16 tile per job:
+  //   L tiles:   L = strictLower(diag(beta) Kc Ki^T); a diagonal tile is inverted
+  //              on the spot (X = (I + L)^-1), the lower-left tile is kept as -L21;
+  //   Mqk tiles: lowerTri(Qc Ki^T).
+  // Four job slots: 0: L00, 1: L11, 2: L10 and Mqk10, 3: Mqk00 and Mqk11.
+  auto tile = [&](Slot<F>& cur, bool is_l, int ti, int tj) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    const u16* arow = is_l ? &sm.Kc[16 * ti + l16][0] : &sm.Qc[16 * ti + l16][0];
+    const u16* brow = &sm.Ki[16 * tj + l16][0];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int kk = 4 * q4 + lg;
-          y = mfma_f32(sm.L[16 + l16][kk], sm.X[kk][l16], y);
-        }
+    for (int ks = 0; ks < F::KS; ++ks) {
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(arow + 32 * ks + 8 * lg);
+      const u32x4_t b = *reinterpret_cast<const u32x4_t*>(brow + 32 * ks + 8 * lg);
+      acc = mfma_k32(a, b, acc);
+    }
+    const int j = 16 * tj + l16;
+    if (!is_l) {
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) sm.Y[4 * lg + ii][l16] = y[ii];
-        wave_lds_sync();
-        f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = 16 * ti + 4 * lg + ii;
+        cur.Mqk[i][j] = to_bf16((j <= i) ? acc[ii] : 0.f);
+      }
+      return;
+    }
+    const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(&cur.beta[16 * ti + 4 * lg]);
+    if (ti != tj) {
+      // lower-left block: every entry is below the diagonal
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int kk = 4 * q4 + lg;
-          z = mfma_f32(sm.X[16 + l16][16 + kk], sm.Y[kk][l16], z);
-        }
+      for (int ii = 0; ii < 4; ++ii) cur.SOL[16 + 4 * lg + ii][j] = to_bf16(-b4[ii] * acc[ii]);
+      return;
+    }
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) cur.INV[16 + 4 * lg + ii][l16] = to_bf16(-z[ii]);
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = 16 * ti + 4 * lg + ii;
+      sm.L[i][j] = (j < i) ? b4[ii] * acc[ii] : 0.f;
+    }
+    // forward substitution of the diagonal block, x_i = [i == m] - sum_{j<i} L_ij x_j
+    // for every column m.  Column m lives in the lane quad 4m..4m+3; quad lane g
+    // owns rows g, g+4, g+8, g+12 and holds those rows of L in registers.  At
+    // step j the finished x_j is broadcast inside each quad (DPP quad_perm) and
+    // every lane updates its four rows; L is zero on and above the diagonal, so
+    // the update needs no masking.
+    wave_lds_sync();
+    const int base = 16 * ti;
+    const int m = lane >> 2;
+    const int gq = lane & 3;
+    float Lr[4][16];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j4 = 0; j4 < 16; j4 += 4) {
+        const f32x4_t w = *reinterpret_cast<const f32x4_t*>(&sm.L[base + gq + 4 * t][base + j4]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Lr[t][j4 + u] = w[u];
+      }
+    float x[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) x[t] = (gq + 4 * t == m) ? 1.f : 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 15; ++jj) {
+      const float xj = quad_bcast(x[jj >> 2], jj & 3);  // x_jj: quad lane jj%4, register jj/4
+#pragma unroll
+      for (int t = 0; t < 4; ++t) x[t] = __builtin_fmaf(-Lr[t][jj], xj, x[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) cur.SOL[base + gq + 4 * t][base + m] = to_bf16(x[t]);
+  };
+  auto chunk_matrices = [&](Slot<F>& cur) {
+    const int jw = wave - F::JOB_BASE;
+    if (jw < 0) return;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k % F::JOB_STRIDE != jw) continue;  // uniform
+      if (k == 0) tile(cur, true, 0, 0);
+      if constexpr (F::CT == 2) {
+        if (k == 1) tile(cur, true, 1, 1);
+        if (k == 2) { tile(cur, true, 1, 0); tile(cur, false, 1, 0); }
+        if (k == 3) { tile(cur, false, 0, 0); tile(cur, false, 1, 1); }
+      } else {
+        if (k == 3) tile(cur, false, 0, 0);
       }
     }
   };
@@ -527,7 +590,10 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       sm.gtc[dst] = __builtin_amdgcn_exp2f(gt - Ca);
     }
   };
-  // B (state): R, U, the state update and the output of the current chunk.
+  // B (state waves): R, the blocked solve for U, the state update and the output
+  // of the current chunk.  With INV = (I + L)^-1 = [[X11, 0], [X21, X22]] the
+  // solve U^T = INV R^T runs as U_top = X11 R_top, U_bot = X22 (R_bot - L21 U_top),
+  // so X21 is never formed.
   auto state_B = [&](Slot<F>& cur) {
     // R^T = diag(beta) (V - P^T), in place in P
 #pragma unroll
@@ -542,57 +608,44 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
           P[ct][nt][ii] = b4[ii] * (bf2f(cur.V[c][vc]) - P[ct][nt][ii]);
         }
     }
-    f32x4_t U[F::CT][F::NTW];
-    if constexpr (F::CT == 2) {
-      u32x4_t bR[F::NTW];
-#pragma unroll
-      for (int nt = 0; nt < F::NTW; ++nt) bR[nt] = acc_pair_to_b(P[0][nt], P[1][nt]);
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const u32x4_t aI = lds_a_pi(&cur.INV[16 * ct + l16][0], 0, lg);
-#pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt)
-          U[ct][nt] = mfma_k32(aI, bR[nt], f32x4_t{0.f, 0.f, 0.f, 0.f});
-      }
-      u32x4_t bU[F::NTW];
-#pragma unroll
-      for (int nt = 0; nt < F::NTW; ++nt) bU[nt] = acc_pair_to_b(U[0][nt], U[1][nt]);
-#pragma unroll
-      for (int kt = 0; kt < F::KT; ++kt) {
-        const f32x4_t av = *reinterpret_cast<const f32x4_t*>(&cur.a[16 * kt + 4 * lg]);
-        const u32x4_t aR = lds_a_tr<F::LDR, true>(&cur.Kr[0][0], 16 * kt, l16, lg);
-#pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt) S[kt][nt] = mfma_k32(aR, bU[nt], S[kt][nt] * av);
-      }
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const u32x4_t aM = lds_a_pi(&cur.Mqk[16 * ct + l16][0], 0, lg);
-#pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt) O[ct][nt] = mfma_k32(aM, bU[nt], O[ct][nt]);
-      }
-    } else {
-      // 16-token chunks: the same 16x16x32 instruction with reduction slots 4-7
-      // zero in both operands (one MFMA shape on every accumulator chain).
-      u32x4_t bR[F::NTW];
-#pragma unroll
-      for (int nt = 0; nt < F::NTW; ++nt) bR[nt] = acc_to_b_pad(P[0][nt]);
-      const u32x4_t aI = lds_a_pad(&cur.INV[l16][0], lg);
+    u32x4_t bU[F::NTW];
+    {
+      const u32x4_t aX11 = lds_a_pad(&cur.SOL[l16][0], lg);
+      f32x4_t Ut[F::NTW];
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt)
-        U[0][nt] = mfma_k32(aI, bR[nt], f32x4_t{0.f, 0.f, 0.f, 0.f});
-      u32x4_t bU[F::NTW];
+        Ut[nt] = mfma_k32(aX11, acc_to_b_pad(P[0][nt]), f32x4_t{0.f, 0.f, 0.f, 0.f});
+      if constexpr (F::CT == 2) {
+        const u32x4_t aNL21 = lds_a_pad(&cur.SOL[16 + l16][0], lg);
+        const u32x4_t aX22 = lds_a_pad(&cur.SOL[16 + l16][16], lg);
 #pragma unroll
-      for (int nt = 0; nt < F::NTW; ++nt) bU[nt] = acc_to_b_pad(U[0][nt]);
+        for (int nt = 0; nt < F::NTW; ++nt) {
+          const u32x4_t bUt = acc_to_b_pad(Ut[nt]);
+          const f32x4_t Tb = mfma_k32(aNL21, bUt, P[1][nt]);  // R_bot - L21 U_top
+          const f32x4_t Ub = mfma_k32(aX22, acc_to_b_pad(Tb), f32x4_t{0.f, 0.f, 0.f, 0.f});
+          bU[nt] = acc_pair_to_b(Ut[nt], Ub);
+        }
+      } else {
 #pragma unroll
-      for (int kt = 0; kt < F::KT; ++kt) {
-        const f32x4_t av = *reinterpret_cast<const f32x4_t*>(&cur.a[16 * kt + 4 * lg]);
-        const u32x4_t aR = lds_a_tr<F::LDR, false>(&cur.Kr[0][0], 16 * kt, l16, lg);
-#pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt) S[kt][nt] = mfma_k32(aR, bU[nt], S[kt][nt] * av);
+        for (int nt = 0; nt < F::NTW; ++nt) bU[nt] = acc_to_b_pad(Ut[nt]);
       }
-      const u32x4_t aM = lds_a_pad(&cur.Mqk[l16][0], lg);
+    }
+    // S^T <- diag(a) S^T + Kr^T U^T
 #pragma unroll
-      for (int nt = 0; nt < F::NTW; ++nt) O[0][nt] = mfma_k32(aM, bU[nt], O[0][nt]);
+    for (int kt = 0; kt < F::KT; ++kt) {
+      const f32x4_t av = *reinterpret_cast<const f32x4_t*>(&cur.a[16 * kt + 4 * lg]);
+      const u32x4_t aR = lds_a_tr<F::LDR, F::CT == 2>(&cur.Kr[0][0], 16 * kt, l16, lg);
+#pragma unroll
+      for (int nt = 0; nt < F::NTW; ++nt) S[kt][nt] = mfma_k32(aR, bU[nt], S[kt][nt] * av);
+    }
+    // O^T = O0^T + Mqk U^T
+#pragma unroll
+    for (int ct = 0; ct < F::CT; ++ct) {
+      u32x4_t aM;
+      if constexpr (F::CT == 2) aM = lds_a_pi(&cur.Mqk[16 * ct + l16][0], 0, lg);
+      else aM = lds_a_pad(&cur.Mqk[l16][0], lg);
+#pragma unroll
+      for (int nt = 0; nt < F::NTW; ++nt) O[ct][nt] = mfma_k32(aM, bU[nt], O[ct][nt]);
     }
     // stage O^T as bf16 [token][value] for coalesced stores
 #pragma unroll
@@ -635,7 +688,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     store_bf16<F::EPT>(&nxt.Kd[r_row][r_col], oKd);
     store_bf16<F::EPT>(&nxt.Kr[r_row][r_col], oKr);
   };
-  // C (state): the staged output of the current chunk, 16 bytes per store; the
+  // C (every wave): the staged output of the current chunk, 16 bytes per store; the
   // descriptor covers the valid rows only, so stores past the sequence are dropped.
   auto store_out = [&](int64_t cur_start, int cur_valid) {
     const __amdgpu_buffer_rsrc_t ro =
@@ -654,81 +707,11 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
                                              0, 0);
     }
   };
-  // D (prep): intra-chunk products and the diagonal inverse blocks.  Job j runs
-  // on wave j % NW; jobs 0..NTRI-1 are L tiles, the rest Mqk tiles; the wave of
-  // each diagonal L tile then inverts that block.
-  auto prep_D = [&](Slot<F>& nxt) {
-    constexpr int NTRI = F::CT * (F::CT + 1) / 2;
-    for (int job = wave; job < 2 * NTRI; job += NW) {
-      const int which = job / NTRI;  // 0: L, 1: Mqk
-      const int tri = job % NTRI;
-      const int ti = tri == 0 ? 0 : 1;
-      const int tj = tri == 2 ? 1 : 0;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      const u16* arow = which ? &sm.Qc[16 * ti + l16][0] : &sm.Kc[16 * ti + l16][0];
-      const u16* brow = &sm.Ki[16 * tj + l16][0];
-#pragma unroll
-      for (int ks = 0; ks < F::KS; ++ks) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(arow + 32 * ks + 8 * lg);
-        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(brow + 32 * ks + 8 * lg);
-        acc = mfma_k32(a, b, acc);
-      }
-      const int j = 16 * tj + l16;
-      if (which == 0) {
-        const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(&nxt.beta[16 * ti + 4 * lg]);
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int i = 16 * ti + 4 * lg + ii;
-          sm.L[i][j] = (j < i) ? b4[ii] * acc[ii] : 0.f;
-        }
-      } else {
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int i = 16 * ti + 4 * lg + ii;
-          nxt.Mqk[i][j] = to_bf16((j <= i) ? acc[ii] : 0.f);
-        }
-      }
-      if (which == 0 && ti == tj) {
-        // forward substitution of the diagonal block, x_i = [i == m] - sum_{j<i} L_ij x_j
-        // for every column m.  Column m lives in the lane quad 4m..4m+3; quad lane g
-        // owns rows g, g+4, g+8, g+12 and holds those rows of L in registers.  At
-        // step j the finished x_j is broadcast inside each quad (DPP quad_perm) and
-        // every lane updates its four rows; L is zero on and above the diagonal, so
-        // the update needs no masking.
-        wave_lds_sync();
-        const int base = 16 * ti;
-        const int m = lane >> 2;
-        const int gq = lane & 3;
-        float Lr[4][16];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int j4 = 0; j4 < 16; j4 += 4) {
-            const f32x4_t w =
-                *reinterpret_cast<const f32x4_t*>(&sm.L[base + gq + 4 * t][base + j4]);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) Lr[t][j4 + u] = w[u];
-          }
-        float x[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) x[t] = (gq + 4 * t == m) ? 1.f : 0.f;
-#pragma unroll
-        for (int j = 0; j < 15; ++j) {
-          // x_j sits in quad lane j % 4, register j / 4
-          const float xj = quad_bcast(x[j >> 2], j & 3);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) x[t] = __builtin_fmaf(-Lr[t][j], xj, x[t]);
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          sm.X[base + gq + 4 * t][base + m] = x[t];
-          nxt.INV[base + gq + 4 * t][base + m] = to_bf16(x[t]);
-        }
-      }
-    }
-  };
 
   // ======================= schedule ==========================================
+  // Step s: state side of chunk s (A: P, O0; B: solve, update, output), the
+  // chunk-local matrices of chunk s (A, job waves) and the preparation of chunk
+  // s+1 (A: gate and norms, B: prefix, C: operands); three LDS-only barriers.
   if (nchunks > 0) {
     // prologue: prepare chunk 0 into slot 0
     load_raw(0);
@@ -739,43 +722,36 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     lds_barrier();
     prep_C(sm.slot[0]);
     lds_barrier();
-    prep_D(sm.slot[0]);
-    lds_barrier();
-    // steady state: state side of chunk s next to the preparation of chunk s+1
     for (int s = 0; s + 1 < nchunks; ++s) {
       Slot<F>& cur = sm.slot[s & 1];
       Slot<F>& nxt = sm.slot[(s + 1) & 1];
-      const int64_t cur_start = s0 + (int64_t)s * C;
       prep_A(nxt, chunk_valid(s + 1));
       load_raw(s + 2 < nchunks ? s + 2 : nchunks - 1);
-      state_A(cur);
-      inv_offdiag(cur);
+      if (is_state) state_A(cur);
+      chunk_matrices(cur);
       lds_barrier();
       prep_B(nxt);
-      state_B(cur);
+      if (is_state) state_B(cur);
       lds_barrier();
       prep_C(nxt);
-      store_out(cur_start, C);
-      lds_barrier();
-      prep_D(nxt);
+      store_out(s0 + (int64_t)s * C, C);
       lds_barrier();
     }
-    // epilogue: state side of the last chunk
+    // epilogue: the last chunk
     {
       const int s = nchunks - 1;
       Slot<F>& cur = sm.slot[s & 1];
-      state_A(cur);
-      inv_offdiag(cur);
+      if (is_state) state_A(cur);
+      chunk_matrices(cur);
       lds_barrier();
-      state_B(cur);
+      if (is_state) state_B(cur);
       lds_barrier();
       store_out(s0 + (int64_t)s * C, chunk_valid(s));
     }
   }
 
   // ---- state out ------------------------------------------------------------
-  if (p.s_out != nullptr) {
-    const int64_t sbase = ((int64_t)n * H + h) * D * D;
+  if (is_state && p.s_out != nullptr) {
 #pragma unroll
     for (int kt = 0; kt < F::KT; ++kt)
 #pragma unroll
@@ -792,31 +768,32 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   }
 }
 
-template <int D, int C, int VT, int NW>
+template <int D, int C, int VT, int NW, int NSW>
 hipError_t launch_one(const KdaParams& p, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.N * p.H * p.n_vtiles;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((kda_fwd_kernel<D, C, VT, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((kda_fwd_kernel<D, C, VT, NW, NSW>), dim3((unsigned)blocks), dim3(NW * 64), 0,
                      stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// (D, chunk, value tile, waves, state waves)
 #define KDA_SCHEDULES(X)  \
-  X(128, 32, 128, 8)      \
-  X(128, 16, 128, 8)      \
-  X(128, 32, 64, 4)       \
-  X(128, 16, 64, 4)       \
-  X(64, 32, 64, 4)        \
-  X(64, 16, 64, 4)        \
-  X(64, 32, 32, 2)        \
-  X(64, 16, 32, 2)        \
-  X(32, 32, 32, 2)        \
-  X(32, 16, 32, 2)
+  X(128, 32, 128, 8, 4)   \
+  X(128, 16, 128, 8, 4)   \
+  X(128, 32, 64, 4, 4)    \
+  X(128, 16, 64, 4, 4)    \
+  X(64, 32, 64, 4, 4)     \
+  X(64, 16, 64, 4, 4)     \
+  X(64, 32, 32, 2, 2)     \
+  X(64, 16, 32, 2, 2)     \
+  X(32, 32, 32, 2, 2)     \
+  X(32, 16, 32, 2, 2)
 
 bool kda_schedule_supported(int D, int chunk, int v_tile) {
-#define KDA_SUPPORTED(d, c, vt, nw) \
+#define KDA_SUPPORTED(d, c, vt, nw, nsw) \
   if (D == d && chunk == c && v_tile == vt) return true;
   KDA_SCHEDULES(KDA_SUPPORTED)
 #undef KDA_SUPPORTED
@@ -824,8 +801,8 @@ bool kda_schedule_supported(int D, int chunk, int v_tile) {
 }
 
 hipError_t launch_kda_fwd(const KdaParams& p, int D, int chunk, int v_tile, hipStream_t stream) {
-#define KDA_LAUNCH(d, c, vt, nw) \
-  if (D == d && chunk == c && v_tile == vt) return launch_one<d, c, vt, nw>(p, stream);
+#define KDA_LAUNCH(d, c, vt, nw, nsw) \
+  if (D == d && chunk == c && v_tile == vt) return launch_one<d, c, vt, nw, nsw>(p, stream);
   KDA_SCHEDULES(KDA_LAUNCH)
 #undef KDA_LAUNCH
   return hipErrorInvalidValue;
