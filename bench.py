@@ -31,7 +31,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6
 METRIC = "prefill tokens/sec (H=96,D=128) + % of MI355X bf16 MFMA peak"
-PMC_PROFILE = os.path.join(ROOT, "profiles", "kda_fwd_batched_pmc.txt")
+PMC_PROFILE_FMT = os.path.join(ROOT, "profiles", "kda_fwd_{}_pmc.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_62_amd", "csrc", f)
                   for f in ("kda_kernel.hip", "kda_params.h")]
 
@@ -60,12 +60,13 @@ def counted_flops(inp) -> int:
     return int(B * T * H * 7 * D * D)
 
 
-def measured_traffic():
+def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when there is none or the kernel source changed since it was taken."""
-    if not os.path.exists(PMC_PROFILE):
+    path = PMC_PROFILE_FMT.format(workload)
+    if not os.path.exists(path):
         return None
-    text = open(PMC_PROFILE).read()
+    text = open(path).read()
     m_hash = re.search(r"kernel_source_hash:\s*(\w+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
@@ -73,34 +74,36 @@ def measured_traffic():
     return float(m_bytes.group(1))
 
 
-def cpu_baseline(inp, heads: int):
-    """Times the fp64 oracle on a sample of heads of the same workload (host cores)."""
-    import oracle
+def cpu_baseline(inp, min_wall: float):
+    """Times the fp64 oracle (the test suite's reference, unchanged) on the same
+    workload on the host cores: whole runs repeated until min_wall seconds passed."""
+    import numpy as np
     import torch
+
+    import oracle
     B, T, H, D = inp["q"].shape
-    hs = list(range(0, H, max(1, H // heads)))[:heads]
-    sel = lambda t: t[:, :, hs].to("cpu")
-    args = [sel(inp[n]) for n in ("q", "k", "v", "g", "beta")]
-    s0 = inp["initial_state"]
-    s0 = None if s0 is None else s0[:, hs].to("cpu")
-    A_log, dt_bias = inp["A_log"][hs].cpu(), inp["dt_bias"][hs].cpu()
-    cu = inp["cu_seqlens"].cpu() if inp["cu_seqlens"] is not None else None
     oracle._load()
     # widen to fp64 outside the timed region, exactly as the oracle would
-    import numpy as np
-    wide = [np.ascontiguousarray(a.to(torch.float64).numpy()) for a in args]
-    s0w = None if s0 is None else np.ascontiguousarray(s0.to(torch.float64).numpy())
+    wide = [np.ascontiguousarray(inp[n].to("cpu", torch.float64).numpy())
+            for n in ("q", "k", "v", "g", "beta")]
+    s0 = inp["initial_state"]
+    s0w = None if s0 is None else np.ascontiguousarray(s0.to("cpu", torch.float64).numpy())
+    A_log = inp["A_log"].to("cpu", torch.float64).numpy()
+    dt_bias = inp["dt_bias"].to("cpu", torch.float64).numpy()
+    cu = inp["cu_seqlens"].cpu() if inp["cu_seqlens"] is not None else None
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    reps = 0
     t0 = time.perf_counter()
-    oracle.kda_fwd(*wide, inp["scale"], A_log.double().numpy(), dt_bias.double().numpy(),
-                   inp["lower_bound"], s0w, cu, nthreads=threads)
-    wall = time.perf_counter() - t0
-    sample_token_heads = B * T * len(hs)
-    return {"value": sample_token_heads / wall / H, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "fp64 per-token recurrence on %d of %d heads (all %d tokens of each), "
-                      "%.2f s wall; tokens/s scaled to all %d heads" % (len(hs), H, B * T, wall,
-                                                                        H)}
+    while True:
+        oracle.kda_fwd(*wide, inp["scale"], A_log, dt_bias, inp["lower_bound"], s0w, cu,
+                       nthreads=threads)
+        reps += 1
+        wall = time.perf_counter() - t0
+        if wall >= min_wall:
+            break
+    return {"value": reps * B * T / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "fp64 per-token recurrence over the whole workload (%d tokens x %d heads), "
+                      "%d run(s) in %.2f s wall on %d threads" % (B * T, H, reps, wall, threads)}
 
 
 def main():
@@ -111,8 +114,8 @@ def main():
     ap.add_argument("--workload", default="batched")
     ap.add_argument("--chunk", type=int, default=None, help="force the chunk size")
     ap.add_argument("--v-tile", type=int, default=0, help="force the value tile")
-    ap.add_argument("--cpu-heads", type=int, default=24,
-                    help="heads of the workload the CPU oracle baseline runs")
+    ap.add_argument("--cpu-seconds", type=float, default=1.0,
+                    help="minimum wall time of the CPU oracle baseline (whole-workload runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a known-size "
@@ -183,20 +186,24 @@ def main():
         "mfma_pct_of_bf16_peak": 100.0 * tflops / MFMA_BF16_PEAK_TFLOPS,
         "kernel_ms": ms_per_launch,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
                      "algorithmic_bytes": nbytes, "counted_tflops": tflops},
         "kernel_source_hash": kernel_source_hash(),
     }
     if args.calib_copy_mb:
-        n = args.calib_copy_mb * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        # One elementwise kernel of known traffic (torch.neg: reads and writes every
+        # byte once) over a source evicted from the caches by a 1 GiB fill first.
+        n = args.calib_copy_mb * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
         dst = torch.empty_like(src)
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        flush.fill_(1)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        result["calib_copy_bytes"] = {"read": n * 4, "write": n * 4}
+        result["calib_copy_bytes"] = {"read": n * 2, "write": n * 2}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_heads)
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
