@@ -18,34 +18,43 @@
 //   5. (I + L)^-1 in fp32 on the 16x16 diagonal blocks (forward substitution);
 //      the lower-left block is applied as a blocked solve in step 6
 //   6. state side, per wave on its own value columns (section 3):
-//        P^T = Kd S^T, O0^T = Qd S^T, R^T = diag(beta)(V - P^T), U^T = (I+L)^-1 R^T,
-//        S^T <- diag(a) S^T + Kr^T U^T,  O^T = O0^T + Mqk U^T
+//        P^T = Kd S^T, O0 = S Qd^T, R^T = diag(beta)(V - P^T), U^T = (I+L)^-1 R^T,
+//        S^T <- diag(a) S^T + Kr^T U^T,  O = O0 + U Mqk^T
 //
 // Schedule.  Steps 1-5 only touch chunk-local data, step 6 is the strictly
 // ordered recurrence (section 3's scheduling property).  Waves 0..NSW-1 hold the
-// state; the other waves prepare.  Step s of the main loop runs three phases
-// separated by workgroup barriers that fence LDS only, so the raw inputs of
-// chunk s+2, loaded into registers during step s, stay in flight across them:
-//   A  gate and norms of s+1 (all) | P, O0 of s (state waves) |
-//      L, Mqk and the diagonal inverse blocks of s (the other waves)
-//   B  prefix scan of s+1 (all)    | R, blocked solve, state update, output of s
-//   C  exponent-scaled operands of s+1 (all) | coalesced store of the output of s
+// state; the others (job waves) run the chunk-local matrix jobs.  Step s of the
+// main loop has two phases separated by workgroup barriers that fence LDS only,
+// so the raw inputs of chunk s+2, loaded into registers during step s, stay in
+// flight:
+//   A  P^T, O0 and the decay of S, then gate and prefix of s+1 (in registers),
+//      then R^T for chunk s (state waves)
+//      | L, Mqk and the diagonal inverse blocks of chunk s, value tile of s+1
+//        (job waves)
+//   B  blocked solve, state update and output of chunk s, stored from registers
+//      (state waves) | norms and exponent-scaled operands of s+1 (every wave)
 // Two LDS slots hold the prepared operands of chunks s and s+1 (the page's
 // prep ring, two deep here).
 //
 // Layout of the state in registers.  Each wave holds S^T (K rows x its value
 // columns) as 16x16 fp32 accumulator tiles: lane l owns value column (l & 15)
 // and key rows 4*(l >> 4) + i, i < 4.  An accumulator tile pair (key rows
-// 32s..32s+31) becomes the bf16 B operand of a 16x16x32 MFMA directly: lane
-// group g = l >> 4 then carries the reduction indices
+// 32s..32s+31) becomes a bf16 operand of a 16x16x32 MFMA directly: lane group
+// g = l >> 4 then carries the reduction indices
 //   pi_g = {32s + 4g + i} U {32s + 16 + 4g + i},  i < 4,
-// and the A operands read from LDS use the same permutation, so the product is
-// exact whatever order the hardware reduces in.  The same holds for the C-long
-// reductions (U, the state update and the output) with the chunk tiles; with
-// 16-token chunks the upper four slots of both operands are zero.  Every bf16
-// product uses the one 16x16x32 shape: a 16x16x16 MFMA that accumulates onto
-// a 16x16x32 result was observed to read part of that accumulator before the
-// first instruction had written it.
+// and the operands read from LDS use the same permutation, so the product is
+// exact whatever order the hardware reduces in.  The A and B operands of the
+// MFMA share one lane layout, so the same packed registers serve either side:
+// P^T = Kd S^T takes S^T as B, O0 = S Qd^T takes it as A, which leaves O with
+// four consecutive values of one token in each lane, ready for an 8-byte store.
+// The q/k-side operands are stored with their key columns already in pi order
+// (position 8g + i holds key 4g + i, position 8g + 4 + i holds key 16 + 4g + i
+// inside each 32-column block), so each operand is one 16-byte LDS read.  The
+// same holds for the C-long reductions (U, the state update and the output)
+// with the chunk tiles; with 16-token chunks the upper four slots of both
+// operands are zero.  Every bf16 product uses the one 16x16x32 shape: a
+// 16x16x16 MFMA that accumulates onto a 16x16x32 result was observed to read
+// part of that accumulator before the first instruction had written it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -81,9 +90,6 @@ __device__ __forceinline__ f32x4_t mfma_k32(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 // Workgroup barrier that orders LDS only: outstanding global loads stay in flight.
 __device__ __forceinline__ void lds_barrier() {
@@ -102,6 +108,11 @@ __device__ __forceinline__ float fast_sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
 }
 
+// Key column held at position p of a pi-ordered row (see the header comment).
+__host__ __device__ constexpr int pi_key(int p) {
+  return (p & ~31) + (((p & 31) >> 3) << 2) + ((p & 4) ? 16 : 0) + (p & 3);
+}
+
 template <int D_, int C_, int VT_, int NW_, int NSW_>
 struct Cfg {
   static constexpr int D = D_;     // key = value head dimension
@@ -114,13 +125,23 @@ struct Cfg {
   static constexpr int KS = D / 32;            // 32-wide steps of D-long reductions
   static constexpr int CT = C / 16;            // 16-row chunk tiles
   static constexpr int NTW = VT / (16 * NSW);  // 16-column value tiles per state wave
-  static constexpr int EPT = C * D / NTHR;     // row-layout elements per thread (q, k, g)
-  static constexpr int TPR = D / EPT;          // threads per chunk row
-  static constexpr int EPV = C * VT / NTHR;    // row-layout elements per thread (v)
-  static constexpr int TPRV = VT / EPV;        // threads per value row
-  static constexpr int SCOLS = D / NW;         // scan columns per wave
-  static constexpr int SPASS = SCOLS / 16;     // scan passes (16 columns x 4 row groups)
-  static constexpr int RPG = C / 4;            // rows per scan group
+  // Role split: with at least four waves beyond the state waves, the state waves
+  // also compute the gate and its prefix while the other waves (job waves) run
+  // the chunk-local matrix jobs and stage the value tile; every wave takes a share
+  // of the exponent-scaled operands.  The two roles run separate loops with the
+  // same barriers.  With fewer waves every wave takes a share of everything in
+  // one loop.
+  static constexpr bool SPLIT = NW - NSW >= 4;
+  static constexpr int JOB_BASE = SPLIT ? NSW : 0;
+  static constexpr int NJW = NW - JOB_BASE;      // job waves (they also stage v and beta)
+  static constexpr int NGW = SPLIT ? NSW : NW;   // gate waves
+  static constexpr int EPT = C * D / NTHR;       // row layout (q, k; every wave): positions per thread
+  static constexpr int TPR = D / EPT;            // threads per chunk row
+  static constexpr int EPV = C * VT / (NJW * 64);  // value row layout (job waves): elements per thread
+  static constexpr int TPRV = VT / EPV;          // threads per value row
+  static constexpr int SCOLS = D / NGW;          // column layout (g; gate waves): key columns per wave
+  static constexpr int SPASS = SCOLS / 16;       // passes of 16 columns: 8 pairs x 8 row groups
+  static constexpr int RPG = C / 8;              // chunk rows per row group
   static constexpr int LDQ = D + 8;            // bf16 row stride of [C][D] tiles
   static constexpr int LDG = D + 4;            // fp32 row stride of the prefix tile
   static constexpr int LDR = D + 16;           // bf16 row stride of the [C][D] Kr tile
@@ -133,54 +154,48 @@ struct Cfg {
   static_assert(EPT == 4 || EPT == 8 || EPT == 16, "row layout");
   static_assert(EPV == 4 || EPV == 8 || EPV == 16, "value row layout");
   static_assert(TPR >= 2 && TPR <= 32, "row reduction: DPP inside rows, one cross-row step");
-  static_assert(SPASS >= 1 && SPASS * 16 * NW == D, "scan layout");
+  static_assert(SPASS >= 1 && SPASS * 16 * NGW == D, "column layout");
   static_assert(D % 32 == 0, "head dim");
-  static_assert(NW >= 2, "two waves for the diagonal inverse blocks");
-  // waves that run the chunk-local matrix jobs: four dedicated ones when there
-  // are enough waves beyond the state waves, otherwise every wave takes some
-  static constexpr int JOB_BASE = (NW - NSW >= 4) ? NSW : 0;
-  static constexpr int JOB_STRIDE = (NW - NSW >= 4) ? 4 : NW;
+  static_assert(NJW == 2 || NJW == 4 || NJW == 8, "job assignment");
+  static_assert(C <= NJW * 64, "one beta per job thread");
 };
+
+// Job wave that runs chunk-local matrix job j (16x16 tiles; 32-token chunks:
+// 0 L00, 1 L11, 2 L10, 3 Mqk10, 4 Mqk00, 5 Mqk11; 16-token chunks: 0 L00, 1 Mqk00).
+// The two diagonal L jobs, which also invert their block, get waves of their own.
+template <int NJW, int CT>
+__device__ constexpr int job_wave(int j) {
+  if (CT == 1) return j % NJW;
+  if (NJW >= 6) return j;
+  if (NJW == 4) return j < 4 ? j : j - 2;
+  return j & 1;
+}
 
 // Prepared operands of one chunk.
 template <class F>
 struct alignas(16) Slot {
-  u16 Qd[F::C][F::LDQ];
-  u16 Kd[F::C][F::LDQ];
-  u16 Kr[F::C][F::LDR];
+  u16 Qd[F::C][F::LDQ];      // pi-ordered key positions
+  u16 Kd[F::C][F::LDQ];      // pi-ordered key positions
+  u16 Kr[F::C][F::LDR];      // natural key order (read transposed)
   u16 SOL[F::C][F::LDC];     // [[X11, 0], [-L21, X22]]: X = (I + L)^-1 diagonal blocks
   u16 Mqk[F::C][F::LDC];
   u16 V[F::C][F::LDV];
   float a[2 * F::D];         // 2^G_T (second half: discarded writes)
-  float beta[F::NTHR];       // sigmoid(beta); entries past the chunk rows unused
+  float beta[F::C];          // sigmoid(beta), zero past the sequence
 };
 
 template <class F>
 struct alignas(16) Smem {
   Slot<F> slot[2];
-  u16 Qc[F::C][F::LDQ];      // centred operands of the chunk being prepared
+  u16 Qc[F::C][F::LDQ];      // centred operands of the chunk being prepared (pi order)
   u16 Kc[F::C][F::LDQ];
   u16 Ki[F::C][F::LDQ];
-  u16 Ost[F::C][F::LDV];     // output staging for coalesced stores
-  float G[F::C][F::LDG];     // base-2 decay, then its inclusive prefix
+  float G[F::C][F::LDG];     // inclusive base-2 decay prefix of the chunk being prepared
   float L[F::C][F::LDL];     // diagonal tiles of strictLower(diag(beta) Kc Ki^T)
   float gtc[2 * F::D];       // 2^(G_T - Ca) (second half: discarded writes)
 };
 
-// Loads N consecutive bf16 (N in {4, 8, 16}) as packed words.
-template <int N>
-__device__ __forceinline__ void load_words(const u16* p, unsigned* w) {
-  if constexpr (N == 4) {
-    u32x2_t x = *reinterpret_cast<const u32x2_t*>(p);
-    w[0] = x[0]; w[1] = x[1];
-  } else {
-#pragma unroll
-    for (int h = 0; h < N / 8; ++h) {
-      u32x4_t x = *reinterpret_cast<const u32x4_t*>(p + 8 * h);
-      w[4 * h] = x[0]; w[4 * h + 1] = x[1]; w[4 * h + 2] = x[2]; w[4 * h + 3] = x[3];
-    }
-  }
-}
+// Stores N consecutive bf16 (N in {4, 8, 16}) from packed words.
 template <int N>
 __device__ __forceinline__ void store_words(u16* p, const unsigned* w) {
   if constexpr (N == 4) {
@@ -201,46 +216,63 @@ __device__ __forceinline__ void store_bf16(u16* p, const float* x) {
   store_words<N>(p, w);
 }
 
-// A operand (16 rows x 32 reductions) of a 16x16x32 MFMA read from a bf16 row-major
-// LDS tile with the pi_g permutation: row r, columns k0 + 4g .. +3 and k0 + 16 + 4g .. +3.
-__device__ __forceinline__ u32x4_t lds_a_pi(const u16* row, int k0, int g) {
-  u32x2_t lo = *reinterpret_cast<const u32x2_t*>(row + k0 + 4 * g);
-  u32x2_t hi = *reinterpret_cast<const u32x2_t*>(row + k0 + 16 + 4 * g);
+// Operand (16 rows x 32 reductions) of a 16x16x32 MFMA from a pi-ordered bf16 LDS
+// row: row r, positions k0 + 8g .. k0 + 8g + 7.
+__device__ __forceinline__ u32x4_t lds_op_pi(const u16* row, int k0, int g) {
+  return *reinterpret_cast<const u32x4_t*>(row + k0 + 8 * g);
+}
+// Operand from a naturally ordered [C][C] bf16 row with the pi_g permutation:
+// columns 4g .. 4g+3 and 16 + 4g .. 16 + 4g + 3.
+__device__ __forceinline__ u32x4_t lds_op_cc(const u16* row, int g) {
+  const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(row + 4 * g);
+  const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(row + 16 + 4 * g);
   return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
 }
-// A operand for a 16-long reduction: row r, columns 4g .. 4g+3, slots 4-7 zero.
-__device__ __forceinline__ u32x4_t lds_a_pad(const u16* row, int g) {
-  u32x2_t lo = *reinterpret_cast<const u32x2_t*>(row + 4 * g);
+// Operand for a 16-long reduction: row r, columns 4g .. 4g+3, slots 4-7 zero.
+__device__ __forceinline__ u32x4_t lds_op_pad(const u16* row, int g) {
+  const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(row + 4 * g);
   return u32x4_t{lo[0], lo[1], 0u, 0u};
 }
-// Transposed A operand from a bf16 row-major [C][ld] tile: MFMA row m = key column
-// k0 + m, reduction slots = chunk rows (pi_g: 4g+i, then 16+4g+i).  Built from LDS
-// transpose reads: inside each 16-lane group, lane i of the result takes element
-// i%4 of the 4-element pieces addressed by lanes i/4, 4+i/4, 8+i/4 and 12+i/4, so
-// lane j addresses row 4g + j/4, columns k0 + 4(j%4) .. +3.
-__device__ __forceinline__ s16x4_t ds_read_tr(const u16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4_t*)(p));
+// Transposed reads from a bf16 row-major [rows][ld] tile.  Inside each 16-lane
+// group, lane i of a ds_read_b64_tr_b16 result takes element i%4 of the 4-element
+// pieces addressed by lanes i/4, 4+i/4, 8+i/4 and 12+i/4; lane j addresses row
+// 4g + j/4, columns k0 + 4(j%4) .. +3.  Lane i of group g so receives column
+// k0 + i of rows 4g .. 4g+3.
+__device__ __forceinline__ u32x2_t ds_read_tr(const u16* p) {
+  return __builtin_bit_cast(
+      u32x2_t,
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p)));
 }
+template <int LD>
+__device__ __forceinline__ u32x2_t lds_col4(const u16* tile, int k0, int l16, int g) {
+  return ds_read_tr(tile + (4 * g + (l16 >> 2)) * LD + k0 + 4 * (l16 & 3));
+}
+// Transposed operand: MFMA row m = column k0 + m, reduction slots = tile rows in
+// pi_g order (4g + i, then 16 + 4g + i; upper slots zero when TWO is false).
 template <int LD, bool TWO>
-__device__ __forceinline__ u32x4_t lds_a_tr(const u16* tile, int k0, int l16, int g) {
-  const u16* p = tile + (4 * g + (l16 >> 2)) * LD + k0 + 4 * (l16 & 3);
-  const u32x2_t lo = __builtin_bit_cast(u32x2_t, ds_read_tr(p));
+__device__ __forceinline__ u32x4_t lds_op_tr(const u16* tile, int k0, int l16, int g) {
+  const u32x2_t lo = lds_col4<LD>(tile, k0, l16, g);
   if constexpr (TWO) {
-    const u32x2_t hi = __builtin_bit_cast(u32x2_t, ds_read_tr(p + 16 * LD));
+    const u32x2_t hi = lds_col4<LD>(tile + 16 * LD, k0, l16, g);
     return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
   } else {
     return u32x4_t{lo[0], lo[1], 0u, 0u};
   }
 }
 
-// Two accumulator tiles (rows 4g+i and 16+4g+i of one 32-row block) -> bf16 B operand.
-__device__ __forceinline__ u32x4_t acc_pair_to_b(f32x4_t t0, f32x4_t t1) {
+// a.lo * b.lo + a.hi * b.hi + c for two packed bf16 pairs (fp32 accumulate).
+__device__ __forceinline__ float dot2_bf16(unsigned a, unsigned b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Two accumulator tiles (rows 4g+i and 16+4g+i of one 32-row block) -> bf16 operand.
+__device__ __forceinline__ u32x4_t acc_pair_to_op(f32x4_t t0, f32x4_t t1) {
   return u32x4_t{pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]), pack_bf16(t1[0], t1[1]),
                  pack_bf16(t1[2], t1[3])};
 }
-// One accumulator tile (rows 4g+i of a 16-row block) -> bf16 B operand, slots 4-7 zero.
-__device__ __forceinline__ u32x4_t acc_to_b_pad(f32x4_t t0) {
+// One accumulator tile (rows 4g+i of a 16-row block) -> bf16 operand, slots 4-7 zero.
+__device__ __forceinline__ u32x4_t acc_to_op_pad(f32x4_t t0) {
   return u32x4_t{pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]), 0u, 0u};
 }
 
@@ -308,7 +340,10 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int l16 = lane & 15;
   const int lg = lane >> 4;
-  const bool is_state = wave < NSW;  // uniform per wave
+  const bool is_state = wave < NSW;            // uniform per wave
+  const bool is_job = wave >= F::JOB_BASE;     // uniform per wave
+  const int jw = is_job ? wave - F::JOB_BASE : 0;        // index among the job waves
+  const int jtid = is_job ? tid - F::JOB_BASE * 64 : 0;  // thread index among them
 
   // ---- work item ---------------------------------------------------------
   const int vt_idx = blockIdx.x % p.n_vtiles;
@@ -327,22 +362,15 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   }
   const int64_t H = p.H;
   const int nchunks = (int)((s1 - s0 + C - 1) / C);
-
-  // ---- per-head constants ------------------------------------------------
-  const float A = __expf(p.A_log[h]);
-  const int r_row = tid / F::TPR;              // chunk row of the row layout (q, k, g)
-  const int r_col = (tid % F::TPR) * F::EPT;   // first key column of the row layout
-  const int v_row = tid / F::TPRV;             // chunk row of the value row layout
-  const int v_col = (tid % F::TPRV) * F::EPV;  // first value column (inside the tile)
-  const float gate_mul = -A * kLog2e;          // sigmoid argument in base 2
-  float gate_add[F::EPT];
-#pragma unroll
-  for (int e = 0; e < F::EPT; ++e) gate_add[e] = gate_mul * p.dt_bias[(int64_t)h * D + r_col + e];
-  const float Ca = p.anchor;
-  const float c1 = __builtin_amdgcn_exp2f(Ca);  // 2^Ca
+  const uint32_t row_bytes = (uint32_t)(H * D * 2);
+  auto chunk_valid = [&](int c) -> int {
+    const int64_t rem = s1 - (s0 + (int64_t)c * C);
+    return rem < C ? (int)rem : C;
+  };
 
   // ---- state in: S^T accumulators of the state waves -------------------------
-  const int vbase = vt_idx * VT + wave * 16 * F::NTW;  // first value row of a state wave
+  const int wv0 = wave * 16 * F::NTW;          // first value column of a state wave (in the tile)
+  const int vbase = vt_idx * VT + wv0;         // ... in the head
   const int64_t sbase = ((int64_t)n * H + h) * D * D;
   f32x4_t S[F::KT][F::NTW];
 #pragma unroll
@@ -373,76 +401,10 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     }
   }
 
-  // ---- raw inputs of the next chunk to prepare, in registers ----------------
-  // Buffer loads through a descriptor bounded to the chunk's valid rows: rows past
-  // the end of the sequence read as zero, without branches.  Offsets are 32-bit
-  // (the host bounds C * H * D * 2 below 2^31).
-  const uint32_t row_bytes = (uint32_t)(H * D * 2);
-  const uint32_t off_qkg = (uint32_t)r_row * row_bytes + (uint32_t)r_col * 2;
-  const uint32_t off_v = (uint32_t)v_row * row_bytes + (uint32_t)(vt_idx * VT + v_col) * 2;
-  const uint32_t off_b = (uint32_t)tid * (uint32_t)(H * 2);
-  unsigned raw_q[F::EPT / 2], raw_k[F::EPT / 2], raw_g[F::EPT / 2], raw_v[F::EPV / 2];
-  unsigned raw_b = 0;
-  auto chunk_valid = [&](int c) -> int {
-    const int64_t rem = s1 - (s0 + (int64_t)c * C);
-    return rem < C ? (int)rem : C;
-  };
-  auto load_raw = [&](int c) {
-    const int64_t cs = s0 + (int64_t)c * C;
-    const int valid = chunk_valid(c);
-    const int64_t tok_elem = (cs * H + h) * D;
-    const int nb = valid * (int)row_bytes;
-    buf_load<F::EPT>(make_rsrc(p.q + tok_elem, nb), off_qkg, raw_q);
-    buf_load<F::EPT>(make_rsrc(p.k + tok_elem, nb), off_qkg, raw_k);
-    buf_load<F::EPT>(make_rsrc(p.g + tok_elem, nb), off_qkg, raw_g);
-    buf_load<F::EPV>(make_rsrc(p.v + tok_elem, nb), off_v, raw_v);
-    raw_b = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(p.beta + cs * H + h, valid * (int)H * 2),
-                                                 off_b, 0, 0);
-  };
-
-  // normalised q, k of the chunk being prepared (row layout), phase A -> phase C
-  float qn[F::EPT], kn[F::EPT];
+  // ======================= state side (state waves) ==========================
   f32x4_t P[F::CT][F::NTW], O[F::CT][F::NTW];
-
-  // ======================= phase bodies ======================================
-  // A (prep, every wave): gate, norms, value tile and beta of the next chunk.
-  auto prep_A = [&](Slot<F>& nxt, int nxt_valid) {
-    const float lbv = r_row < nxt_valid ? p.lb2 : 0.f;  // rows past the sequence: no decay
-    float gv[F::EPT];
-#pragma unroll
-    for (int e = 0; e < F::EPT / 2; ++e) {
-      qn[2 * e] = bflo(raw_q[e]); qn[2 * e + 1] = bfhi(raw_q[e]);
-      kn[2 * e] = bflo(raw_k[e]); kn[2 * e + 1] = bfhi(raw_k[e]);
-      gv[2 * e] = bflo(raw_g[e]); gv[2 * e + 1] = bfhi(raw_g[e]);
-    }
-    float sq = 0.f, sk = 0.f;
-#pragma unroll
-    for (int e = 0; e < F::EPT; ++e) {
-      sq = __builtin_fmaf(qn[e], qn[e], sq);
-      sk = __builtin_fmaf(kn[e], kn[e], sk);
-    }
-    sq = group_sum<F::TPR>(sq);
-    sk = group_sum<F::TPR>(sk);
-    const float rq = p.scale * __builtin_amdgcn_rsqf(sq + kNormEps);
-    const float rk = __builtin_amdgcn_rsqf(sk + kNormEps);
-    float lam[F::EPT];
-#pragma unroll
-    for (int e = 0; e < F::EPT; ++e) {
-      qn[e] *= rq;
-      kn[e] *= rk;
-      const float sg = __builtin_amdgcn_rcpf(
-          1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(gv[e], gate_mul, gate_add[e])));
-      lam[e] = lbv * sg;
-    }
-#pragma unroll
-    for (int e = 0; e < F::EPT; e += 4)
-      *reinterpret_cast<f32x4_t*>(&sm.G[r_row][r_col + e]) =
-          f32x4_t{lam[e], lam[e + 1], lam[e + 2], lam[e + 3]};
-    store_words<F::EPV>(&nxt.V[v_row][v_col], raw_v);
-    // every thread writes its slot entry; entries past the chunk rows are unused
-    nxt.beta[tid] = tid < nxt_valid ? fast_sigmoid(bf2f((u16)raw_b)) : 0.f;
-  };
-  // A (state waves): P^T = Kd S^T and O0^T = Qd S^T.
+  // A: P^T = Kd S^T and O0 = S Qd^T with the decay S^T <- diag(a) S^T alongside
+  // (state_A), then R^T = diag(beta)(V - P^T) in place in P (state_R).
   auto state_A = [&](Slot<F>& cur) {
 #pragma unroll
     for (int ct = 0; ct < F::CT; ++ct)
@@ -451,41 +413,297 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
         P[ct][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         O[ct][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
-    // one 32-row key step at a time: its bf16 copy of S^T is live only there
+    // one 32-row key step at a time: its bf16 copy of S^T is live only there, and
+    // once it is taken the decay of those rows proceeds while the products run
 #pragma unroll
     for (int ks = 0; ks < F::KS; ++ks) {
       u32x4_t bS[F::NTW];
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt)
-        bS[nt] = acc_pair_to_b(S[2 * ks][nt], S[2 * ks + 1][nt]);
+        bS[nt] = acc_pair_to_op(S[2 * ks][nt], S[2 * ks + 1][nt]);
+      const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(&cur.a[32 * ks + 4 * lg]);
+      const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(&cur.a[32 * ks + 16 + 4 * lg]);
+#pragma unroll
+      for (int nt = 0; nt < F::NTW; ++nt) {
+        S[2 * ks][nt] *= a0;
+        S[2 * ks + 1][nt] *= a1;
+      }
 #pragma unroll
       for (int ct = 0; ct < F::CT; ++ct) {
-        const u32x4_t aK = lds_a_pi(&cur.Kd[16 * ct + l16][0], 32 * ks, lg);
-        const u32x4_t aQ = lds_a_pi(&cur.Qd[16 * ct + l16][0], 32 * ks, lg);
+        const u32x4_t aK = lds_op_pi(&cur.Kd[16 * ct + l16][0], 32 * ks, lg);
+        const u32x4_t aQ = lds_op_pi(&cur.Qd[16 * ct + l16][0], 32 * ks, lg);
 #pragma unroll
         for (int nt = 0; nt < F::NTW; ++nt) {
           P[ct][nt] = mfma_k32(aK, bS[nt], P[ct][nt]);
-          O[ct][nt] = mfma_k32(aQ, bS[nt], O[ct][nt]);
+          O[ct][nt] = mfma_k32(bS[nt], aQ, O[ct][nt]);
         }
       }
     }
   };
-  // A (job waves): the chunk-local matrices of the current chunk from its centred
-  // operands.  One 16x16 tile per job:
+  auto state_R = [&](Slot<F>& cur) {
+#pragma unroll
+    for (int ct = 0; ct < F::CT; ++ct) {
+      const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(&cur.beta[16 * ct + 4 * lg]);
+#pragma unroll
+      for (int nt = 0; nt < F::NTW; ++nt) {
+        // lane: value column wv0 + 16 nt + l16, chunk rows 16 ct + 4 lg .. +3
+        const u32x2_t vv = lds_col4<F::LDV>(&cur.V[16 * ct][0], wv0 + 16 * nt, l16, lg);
+        P[ct][nt][0] = b4[0] * (bflo(vv[0]) - P[ct][nt][0]);
+        P[ct][nt][1] = b4[1] * (bfhi(vv[0]) - P[ct][nt][1]);
+        P[ct][nt][2] = b4[2] * (bflo(vv[1]) - P[ct][nt][2]);
+        P[ct][nt][3] = b4[3] * (bfhi(vv[1]) - P[ct][nt][3]);
+      }
+    }
+  };
+  // B: the blocked solve for U, the state update and the output of the current
+  // chunk.  With INV = (I + L)^-1 = [[X11, 0], [X21, X22]] the solve U^T = INV R^T
+  // runs as U_top = X11 R_top, U_bot = X22 (R_bot - L21 U_top), so X21 is never
+  // formed.  The output leaves as bf16 straight from the accumulators, through a
+  // descriptor bounded to the chunk's valid rows.
+  auto state_B = [&](Slot<F>& cur, int64_t cur_start, int cur_valid) {
+    u32x4_t bU[F::NTW];
+    {
+      const u32x4_t aX11 = lds_op_pad(&cur.SOL[l16][0], lg);
+      f32x4_t Ut[F::NTW];
+#pragma unroll
+      for (int nt = 0; nt < F::NTW; ++nt)
+        Ut[nt] = mfma_k32(aX11, acc_to_op_pad(P[0][nt]), f32x4_t{0.f, 0.f, 0.f, 0.f});
+      if constexpr (F::CT == 2) {
+        const u32x4_t aNL21 = lds_op_pad(&cur.SOL[16 + l16][0], lg);
+        const u32x4_t aX22 = lds_op_pad(&cur.SOL[16 + l16][16], lg);
+#pragma unroll
+        for (int nt = 0; nt < F::NTW; ++nt) {
+          const f32x4_t Tb = mfma_k32(aNL21, acc_to_op_pad(Ut[nt]), P[1][nt]);  // R_bot - L21 U_top
+          const f32x4_t Ub = mfma_k32(aX22, acc_to_op_pad(Tb), f32x4_t{0.f, 0.f, 0.f, 0.f});
+          bU[nt] = acc_pair_to_op(Ut[nt], Ub);
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < F::NTW; ++nt) bU[nt] = acc_to_op_pad(Ut[nt]);
+      }
+    }
+    // S^T += Kr^T U^T (the decay was applied in phase A)
+#pragma unroll
+    for (int kt = 0; kt < F::KT; ++kt) {
+      const u32x4_t aR = lds_op_tr<F::LDR, F::CT == 2>(&cur.Kr[0][0], 16 * kt, l16, lg);
+#pragma unroll
+      for (int nt = 0; nt < F::NTW; ++nt) S[kt][nt] = mfma_k32(aR, bU[nt], S[kt][nt]);
+    }
+    // O = O0 + U Mqk^T: U as the A operand (value rows), Mqk rows as B (token columns)
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(p.out + (cur_start * H + h) * D + vt_idx * VT, cur_valid * (int)row_bytes);
+#pragma unroll
+    for (int ct = 0; ct < F::CT; ++ct) {
+      u32x4_t bM;
+      if constexpr (F::CT == 2) bM = lds_op_cc(&cur.Mqk[16 * ct + l16][0], lg);
+      else bM = lds_op_pad(&cur.Mqk[l16][0], lg);
+#pragma unroll
+      for (int nt = 0; nt < F::NTW; ++nt) {
+        const f32x4_t o = mfma_k32(bU[nt], bM, O[ct][nt]);
+        // lane: token 16 ct + l16, values wv0 + 16 nt + 4 lg .. +3
+        const u32x2_t w = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(
+            w, ro, (uint32_t)(16 * ct + l16) * row_bytes + (uint32_t)(wv0 + 16 * nt + 4 * lg) * 2,
+            0, 0);
+      }
+    }
+  };
+
+  // ======================= preparation ======================================
+  // Column layout (g, gate, prefix; gate waves): pass ps covers key columns
+  // g_col0 + 16 ps and g_col0 + 16 ps + 1 (lane bits 0-2 pick the pair) and chunk
+  // rows g_row0 .. g_row0 + RPG - 1 (lane bits 3-5 pick one of eight row groups).
+  const int g_col0 = wave * F::SCOLS + 2 * (lane & 7);
+  const int g_rg = lane >> 3;
+  const int g_row0 = g_rg * F::RPG;
+  // Row layout (q, k, operands; every wave): chunk row r_row, positions r_col ..
+  // r_col + EPT - 1.
+  const int r_row = tid / F::TPR;
+  const int r_col = (tid % F::TPR) * F::EPT;
+  // Value row layout (job waves).
+  const int v_row = jtid / F::TPRV;
+  const int v_col = (jtid % F::TPRV) * F::EPV;
+  const float A = __expf(p.A_log[h]);
+  const float gate_mul = -A * kLog2e;  // sigmoid argument in base 2
+  float gate_add[F::SPASS][2];
+#pragma unroll
+  for (int ps = 0; ps < F::SPASS; ++ps)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      gate_add[ps][c] = gate_mul * p.dt_bias[(int64_t)h * D + g_col0 + 16 * ps + c];
+  const float Ca = p.anchor;
+  const float c1 = __builtin_amdgcn_exp2f(Ca);  // 2^Ca
+
+  // Raw inputs of the chunk to prepare next, in registers.  Buffer loads through a
+  // descriptor bounded to the chunk's valid rows: rows past the end of the
+  // sequence read as zero, without branches.  Offsets are 32-bit (the host bounds
+  // C * H * D * 2 below 2^31).
+  const uint32_t off_qk = (uint32_t)r_row * row_bytes;
+  const uint32_t off_v = (uint32_t)v_row * row_bytes + (uint32_t)(vt_idx * VT + v_col) * 2;
+  const uint32_t off_g = (uint32_t)g_row0 * row_bytes + (uint32_t)g_col0 * 2;
+  const uint32_t off_b = (uint32_t)jtid * (uint32_t)(H * 2);
+  constexpr int NP = F::EPT / 4;  // 4-key pieces per thread in the row layout
+  u32x2_t raw_q[NP], raw_k[NP];
+  unsigned raw_v[F::EPV / 2];
+  unsigned raw_g[F::SPASS][F::RPG];
+  unsigned raw_b = 0;
+  // g (gate waves), v and beta (job waves): consumed in phase A
+  auto load_g = [&](int c) {
+    const int64_t tok_elem = ((s0 + (int64_t)c * C) * H + h) * D;
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g + tok_elem, chunk_valid(c) * (int)row_bytes);
+#pragma unroll
+    for (int ps = 0; ps < F::SPASS; ++ps)
+#pragma unroll
+      for (int i = 0; i < F::RPG; ++i)
+        raw_g[ps][i] = __builtin_amdgcn_raw_buffer_load_b32(
+            rg, off_g + (uint32_t)i * row_bytes + 32u * ps, 0, 0);
+  };
+  auto load_vb = [&](int c) {
+    const int64_t cs = s0 + (int64_t)c * C;
+    const int valid = chunk_valid(c);
+    const int64_t tok_elem = (cs * H + h) * D;
+    buf_load<F::EPV>(make_rsrc(p.v + tok_elem, valid * (int)row_bytes), off_v, raw_v);
+    raw_b = __builtin_amdgcn_raw_buffer_load_b16(
+        make_rsrc(p.beta + cs * H + h, valid * (int)H * 2), off_b, 0, 0);
+  };
+  // q and k: consumed in phase B
+  auto load_qk = [&](int c) {
+    const int64_t cs = s0 + (int64_t)c * C;
+    const int64_t tok_elem = (cs * H + h) * D;
+    const int nb = chunk_valid(c) * (int)row_bytes;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + tok_elem, nb);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + tok_elem, nb);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const uint32_t o = off_qk + (uint32_t)pi_key(r_col + 4 * j) * 2;
+      raw_q[j] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rq, o, 0, 0));
+      raw_k[j] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rk, o, 0, 0));
+    }
+  };
+  // Exclusive prefix over the eight row groups (lanes c, c+8, ..., c+56) of a
+  // per-lane total t.  Row groups 2r and 2r+1 share the 16-lane row r: a DPP
+  // shift by 8 inside the row gives the odd group its even neighbour, a rotate by 8
+  // gives both the row total; the four row totals are then combined across rows
+  // with the lane-swap instructions (the 16-row swap gives [r0, r0, r2, r2] and
+  // [r1, r1, r3, r3]; their sum swapped across the 32-lane halves gives r0 + r1
+  // to rows 2 and 3).
+  auto rowgroup_excl = [&](float t) -> float {
+    const float in_row = __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t), 0x118, 0xf, 0xf, true));
+    const float rt = t + dpp_f<0x128>(t);
+    const unsigned ab = __builtin_bit_cast(unsigned, rt);
+    const auto sw16 = __builtin_amdgcn_permlane16_swap(ab, ab, false, false);
+    const float below = __builtin_bit_cast(float, (unsigned)sw16[0]);  // row r-1 for odd r
+    const float pair = below + __builtin_bit_cast(float, (unsigned)sw16[1]);
+    const unsigned pb = __builtin_bit_cast(unsigned, pair);
+    const auto sw32 = __builtin_amdgcn_permlane32_swap(pb, pb, false, false);
+    const float lower = __builtin_bit_cast(float, (unsigned)sw32[0]);  // r0 + r1
+    return in_row + ((lg & 1) ? below : 0.f) + (lg >= 2 ? lower : 0.f);
+  };
+  // A (gate waves): gate and inclusive prefix of the next chunk (column layout).
+  auto gate = [&](Slot<F>& nxt, int nxt_valid) {
+#pragma unroll
+    for (int ps = 0; ps < F::SPASS; ++ps) {
+      const int col = g_col0 + 16 * ps;
+      float run0[F::RPG], run1[F::RPG];
+      float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < F::RPG; ++i) {
+        const float lbv = g_row0 + i < nxt_valid ? p.lb2 : 0.f;  // no decay past the sequence
+        const float z0 = __builtin_fmaf(bflo(raw_g[ps][i]), gate_mul, gate_add[ps][0]);
+        const float z1 = __builtin_fmaf(bfhi(raw_g[ps][i]), gate_mul, gate_add[ps][1]);
+        t0 = __builtin_fmaf(lbv, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z0)), t0);
+        t1 = __builtin_fmaf(lbv, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z1)), t1);
+        run0[i] = t0;
+        run1[i] = t1;
+      }
+      const float off0 = rowgroup_excl(t0);
+      const float off1 = rowgroup_excl(t1);
+#pragma unroll
+      for (int i = 0; i < F::RPG; ++i)
+        *reinterpret_cast<f32x2_t*>(&sm.G[g_row0 + i][col]) = f32x2_t{run0[i] + off0, run1[i] + off1};
+      // G_T is the last row, held by row group 7; the other groups write the same
+      // expressions into a discarded half of each array (no branch).
+      const float gt0 = t0 + off0, gt1 = t1 + off1;
+      const int dst = (g_rg == 7) ? col : F::D + col;
+      *reinterpret_cast<f32x2_t*>(&nxt.a[dst]) =
+          f32x2_t{__builtin_amdgcn_exp2f(gt0), __builtin_amdgcn_exp2f(gt1)};
+      *reinterpret_cast<f32x2_t*>(&sm.gtc[dst]) =
+          f32x2_t{__builtin_amdgcn_exp2f(gt0 - Ca), __builtin_amdgcn_exp2f(gt1 - Ca)};
+    }
+  };
+  // A (job waves): value tile and beta of the next chunk.
+  auto stage_vb = [&](Slot<F>& nxt, int nxt_valid) {
+    store_words<F::EPV>(&nxt.V[v_row][v_col], raw_v);
+    if (jtid < C) nxt.beta[jtid] = jtid < nxt_valid ? fast_sigmoid(bf2f((u16)raw_b)) : 0.f;
+  };
+  // B: norms and exponent-scaled operands of the next chunk.  Position 4j + e of
+  // this thread's run holds key pi_key(r_col + 4j) + e.
+  auto prep_B = [&](Slot<F>& nxt) {
+    float qn[F::EPT], kn[F::EPT];
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      qn[4 * j] = bflo(raw_q[j][0]); qn[4 * j + 1] = bfhi(raw_q[j][0]);
+      qn[4 * j + 2] = bflo(raw_q[j][1]); qn[4 * j + 3] = bfhi(raw_q[j][1]);
+      kn[4 * j] = bflo(raw_k[j][0]); kn[4 * j + 1] = bfhi(raw_k[j][0]);
+      kn[4 * j + 2] = bflo(raw_k[j][1]); kn[4 * j + 3] = bfhi(raw_k[j][1]);
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        sq = dot2_bf16(raw_q[j][w], raw_q[j][w], sq);
+        sk = dot2_bf16(raw_k[j][w], raw_k[j][w], sk);
+      }
+    }
+    sq = group_sum<F::TPR>(sq);
+    sk = group_sum<F::TPR>(sk);
+    const float rq = p.scale * __builtin_amdgcn_rsqf(sq + kNormEps);
+    const float rk = __builtin_amdgcn_rsqf(sk + kNormEps);
+    // eight positions (one 16-byte store per operand) at a time
+    constexpr int RUN = F::EPT < 8 ? F::EPT : 8;
+#pragma unroll
+    for (int r0 = 0; r0 < F::EPT; r0 += RUN) {
+      float oQc[RUN], oKc[RUN], oKi[RUN], oQd[RUN], oKd[RUN], oKr[RUN];
+#pragma unroll
+      for (int j = 0; j < RUN / 4; ++j) {
+        const int key = pi_key(r_col + r0 + 4 * j);
+        const f32x4_t gg = *reinterpret_cast<const f32x4_t*>(&sm.G[r_row][key]);
+        const f32x4_t tt = *reinterpret_cast<const f32x4_t*>(&sm.gtc[key]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int x = 4 * j + e;
+          const float qv = qn[r0 + x] * rq, kv = kn[r0 + x] * rk;
+          const float d = gg[e] - Ca;
+          const float e1 = __builtin_amdgcn_exp2f(d);   // 2^(G - Ca)
+          const float e2 = __builtin_amdgcn_exp2f(-d);  // 2^(Ca - G)
+          const float ed = e1 * c1;                     // 2^G
+          oQc[x] = qv * e1;
+          oKc[x] = kv * e1;
+          oKi[x] = kv * e2;
+          oQd[x] = qv * ed;
+          oKd[x] = kv * ed;
+          oKr[x] = oKi[x] * tt[e];                      // kh 2^(G_T - G)
+        }
+        store_bf16<4>(&nxt.Kr[r_row][key], &oKr[4 * j]);
+      }
+      store_bf16<RUN>(&sm.Qc[r_row][r_col + r0], oQc);
+      store_bf16<RUN>(&sm.Kc[r_row][r_col + r0], oKc);
+      store_bf16<RUN>(&sm.Ki[r_row][r_col + r0], oKi);
+      store_bf16<RUN>(&nxt.Qd[r_row][r_col + r0], oQd);
+      store_bf16<RUN>(&nxt.Kd[r_row][r_col + r0], oKd);
+    }
+  };
+  // A: the chunk-local matrices of the current chunk from its centred operands,
+  // one 16x16 tile per job:
   //   L tiles:   L = strictLower(diag(beta) Kc Ki^T); a diagonal tile is inverted
   //              on the spot (X = (I + L)^-1), the lower-left tile is kept as -L21;
   //   Mqk tiles: lowerTri(Qc Ki^T).
-  // Four job slots: 0: L00, 1: L11, 2: L10 and Mqk10, 3: Mqk00 and Mqk11.
   auto tile = [&](Slot<F>& cur, bool is_l, int ti, int tj) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     const u16* arow = is_l ? &sm.Kc[16 * ti + l16][0] : &sm.Qc[16 * ti + l16][0];
     const u16* brow = &sm.Ki[16 * tj + l16][0];
 #pragma unroll
-    for (int ks = 0; ks < F::KS; ++ks) {
-      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(arow + 32 * ks + 8 * lg);
-      const u32x4_t b = *reinterpret_cast<const u32x4_t*>(brow + 32 * ks + 8 * lg);
-      acc = mfma_k32(a, b, acc);
-    }
+    for (int ks = 0; ks < F::KS; ++ks)
+      acc = mfma_k32(lds_op_pi(arow, 32 * ks, lg), lds_op_pi(brow, 32 * ks, lg), acc);
     const int j = 16 * tj + l16;
     if (!is_l) {
 #pragma unroll
@@ -539,214 +757,122 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     for (int t = 0; t < 4; ++t) cur.SOL[base + gq + 4 * t][base + m] = to_bf16(x[t]);
   };
   auto chunk_matrices = [&](Slot<F>& cur) {
-    const int jw = wave - F::JOB_BASE;
-    if (jw < 0) return;
+    if constexpr (F::CT == 2) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (k % F::JOB_STRIDE != jw) continue;  // uniform
-      if (k == 0) tile(cur, true, 0, 0);
-      if constexpr (F::CT == 2) {
-        if (k == 1) tile(cur, true, 1, 1);
-        if (k == 2) { tile(cur, true, 1, 0); tile(cur, false, 1, 0); }
-        if (k == 3) { tile(cur, false, 0, 0); tile(cur, false, 1, 1); }
-      } else {
-        if (k == 3) tile(cur, false, 0, 0);
-      }
-    }
-  };
-  // B (prep): inclusive prefix over the chunk rows.  Each wave scans SCOLS columns
-  // as 16 columns x 4 row groups; group offsets are combined across lanes.
-  auto prep_B = [&](Slot<F>& nxt) {
-#pragma unroll
-    for (int ps = 0; ps < F::SPASS; ++ps) {
-      const int col = wave * F::SCOLS + 16 * ps + l16;
-      const int r0 = lg * F::RPG;
-      float run[F::RPG];
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < F::RPG; ++i) {
-        acc += sm.G[r0 + i][col];
-        run[i] = acc;
-      }
-      // Exclusive prefix of the four group totals r0..r3 (one per 16-lane row) with
-      // the lane-swap instructions: the 16-row swap gives [r0, r0, r2, r2] and
-      // [r1, r1, r3, r3]; their sum swapped across the 32-lane halves gives r0 + r1
-      // to rows 2 and 3.
-      const unsigned ab = __builtin_bit_cast(unsigned, acc);
-      const auto sw16 = __builtin_amdgcn_permlane16_swap(ab, ab, false, false);
-      const float below = __builtin_bit_cast(float, (unsigned)sw16[0]);  // row g-1 for odd g
-      const float pair = below + __builtin_bit_cast(float, (unsigned)sw16[1]);
-      const unsigned pb = __builtin_bit_cast(unsigned, pair);
-      const auto sw32 = __builtin_amdgcn_permlane32_swap(pb, pb, false, false);
-      const float lower = __builtin_bit_cast(float, (unsigned)sw32[0]);  // r0 + r1
-      const float off = ((lg & 1) ? below : 0.f) + (lg >= 2 ? lower : 0.f);
-#pragma unroll
-      for (int i = 0; i < F::RPG; ++i) sm.G[r0 + i][col] = run[i] + off;
-      // G_T is the last row, held by lane group 3; the other groups write the
-      // same expressions into a discarded half of each array (no branch).
-      const float gt = run[F::RPG - 1] + off;
-      const int dst = (lg == 3) ? col : F::D + col;
-      nxt.a[dst] = __builtin_amdgcn_exp2f(gt);
-      sm.gtc[dst] = __builtin_amdgcn_exp2f(gt - Ca);
-    }
-  };
-  // B (state waves): R, the blocked solve for U, the state update and the output
-  // of the current chunk.  With INV = (I + L)^-1 = [[X11, 0], [X21, X22]] the
-  // solve U^T = INV R^T runs as U_top = X11 R_top, U_bot = X22 (R_bot - L21 U_top),
-  // so X21 is never formed.
-  auto state_B = [&](Slot<F>& cur) {
-    // R^T = diag(beta) (V - P^T), in place in P
-#pragma unroll
-    for (int ct = 0; ct < F::CT; ++ct) {
-      const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(&cur.beta[16 * ct + 4 * lg]);
-#pragma unroll
-      for (int nt = 0; nt < F::NTW; ++nt)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int c = 16 * ct + 4 * lg + ii;
-          const int vc = wave * 16 * F::NTW + 16 * nt + l16;
-          P[ct][nt][ii] = b4[ii] * (bf2f(cur.V[c][vc]) - P[ct][nt][ii]);
+      for (int j = 0; j < 6; ++j) {
+        if (job_wave<F::NJW, 2>(j) != jw) continue;  // uniform
+        switch (j) {
+          case 0: tile(cur, true, 0, 0); break;
+          case 1: tile(cur, true, 1, 1); break;
+          case 2: tile(cur, true, 1, 0); break;
+          case 3: tile(cur, false, 1, 0); break;
+          case 4: tile(cur, false, 0, 0); break;
+          default: tile(cur, false, 1, 1); break;
         }
-    }
-    u32x4_t bU[F::NTW];
-    {
-      const u32x4_t aX11 = lds_a_pad(&cur.SOL[l16][0], lg);
-      f32x4_t Ut[F::NTW];
-#pragma unroll
-      for (int nt = 0; nt < F::NTW; ++nt)
-        Ut[nt] = mfma_k32(aX11, acc_to_b_pad(P[0][nt]), f32x4_t{0.f, 0.f, 0.f, 0.f});
-      if constexpr (F::CT == 2) {
-        const u32x4_t aNL21 = lds_a_pad(&cur.SOL[16 + l16][0], lg);
-        const u32x4_t aX22 = lds_a_pad(&cur.SOL[16 + l16][16], lg);
-#pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt) {
-          const u32x4_t bUt = acc_to_b_pad(Ut[nt]);
-          const f32x4_t Tb = mfma_k32(aNL21, bUt, P[1][nt]);  // R_bot - L21 U_top
-          const f32x4_t Ub = mfma_k32(aX22, acc_to_b_pad(Tb), f32x4_t{0.f, 0.f, 0.f, 0.f});
-          bU[nt] = acc_pair_to_b(Ut[nt], Ub);
-        }
-      } else {
-#pragma unroll
-        for (int nt = 0; nt < F::NTW; ++nt) bU[nt] = acc_to_b_pad(Ut[nt]);
       }
-    }
-    // S^T <- diag(a) S^T + Kr^T U^T
-#pragma unroll
-    for (int kt = 0; kt < F::KT; ++kt) {
-      const f32x4_t av = *reinterpret_cast<const f32x4_t*>(&cur.a[16 * kt + 4 * lg]);
-      const u32x4_t aR = lds_a_tr<F::LDR, F::CT == 2>(&cur.Kr[0][0], 16 * kt, l16, lg);
-#pragma unroll
-      for (int nt = 0; nt < F::NTW; ++nt) S[kt][nt] = mfma_k32(aR, bU[nt], S[kt][nt] * av);
-    }
-    // O^T = O0^T + Mqk U^T
-#pragma unroll
-    for (int ct = 0; ct < F::CT; ++ct) {
-      u32x4_t aM;
-      if constexpr (F::CT == 2) aM = lds_a_pi(&cur.Mqk[16 * ct + l16][0], 0, lg);
-      else aM = lds_a_pad(&cur.Mqk[l16][0], lg);
-#pragma unroll
-      for (int nt = 0; nt < F::NTW; ++nt) O[ct][nt] = mfma_k32(aM, bU[nt], O[ct][nt]);
-    }
-    // stage O^T as bf16 [token][value] for coalesced stores
-#pragma unroll
-    for (int ct = 0; ct < F::CT; ++ct)
-#pragma unroll
-      for (int nt = 0; nt < F::NTW; ++nt)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          sm.Ost[16 * ct + 4 * lg + ii][wave * 16 * F::NTW + 16 * nt + l16] =
-              to_bf16(O[ct][nt][ii]);
-  };
-  // C (prep): exponent-scaled operands of the next chunk.
-  auto prep_C = [&](Slot<F>& nxt) {
-    float oQc[F::EPT], oKc[F::EPT], oKi[F::EPT], oQd[F::EPT], oKd[F::EPT], oKr[F::EPT];
-    float gv[F::EPT], gt[F::EPT];
-#pragma unroll
-    for (int e = 0; e < F::EPT; e += 4) {
-      const f32x4_t gg = *reinterpret_cast<const f32x4_t*>(&sm.G[r_row][r_col + e]);
-      const f32x4_t tt = *reinterpret_cast<const f32x4_t*>(&sm.gtc[r_col + e]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { gv[e + j] = gg[j]; gt[e + j] = tt[j]; }
-    }
-#pragma unroll
-    for (int e = 0; e < F::EPT; ++e) {
-      const float d = gv[e] - Ca;
-      const float e1 = __builtin_amdgcn_exp2f(d);   // 2^(G - Ca)
-      const float e2 = __builtin_amdgcn_exp2f(-d);  // 2^(Ca - G)
-      const float ed = e1 * c1;                     // 2^G
-      oQc[e] = qn[e] * e1;
-      oKc[e] = kn[e] * e1;
-      oKi[e] = kn[e] * e2;
-      oQd[e] = qn[e] * ed;
-      oKd[e] = kn[e] * ed;
-      oKr[e] = oKi[e] * gt[e];                      // kh 2^(G_T - G)
-    }
-    store_bf16<F::EPT>(&sm.Qc[r_row][r_col], oQc);
-    store_bf16<F::EPT>(&sm.Kc[r_row][r_col], oKc);
-    store_bf16<F::EPT>(&sm.Ki[r_row][r_col], oKi);
-    store_bf16<F::EPT>(&nxt.Qd[r_row][r_col], oQd);
-    store_bf16<F::EPT>(&nxt.Kd[r_row][r_col], oKd);
-    store_bf16<F::EPT>(&nxt.Kr[r_row][r_col], oKr);
-  };
-  // C (every wave): the staged output of the current chunk, 16 bytes per store; the
-  // descriptor covers the valid rows only, so stores past the sequence are dropped.
-  auto store_out = [&](int64_t cur_start, int cur_valid) {
-    const __amdgpu_buffer_rsrc_t ro =
-        make_rsrc(p.out + (cur_start * H + h) * D + vt_idx * VT, cur_valid * (int)row_bytes);
-    constexpr int NPC = C * VT / 8;
-#pragma unroll
-    for (int it = 0; it < (NPC + F::NTHR - 1) / F::NTHR; ++it) {
-      const int pc = tid + it * F::NTHR;
-      if constexpr (NPC % F::NTHR != 0) {
-        if (pc >= NPC) break;
-      }
-      const int row = pc / (VT / 8);
-      const int col = (pc % (VT / 8)) * 8;
-      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(&sm.Ost[row][col]);
-      __builtin_amdgcn_raw_buffer_store_b128(w, ro, (uint32_t)row * row_bytes + (uint32_t)col * 2,
-                                             0, 0);
+    } else {
+      if (job_wave<F::NJW, 1>(0) == jw) tile(cur, true, 0, 0);
+      if (job_wave<F::NJW, 1>(1) == jw) tile(cur, false, 0, 0);
     }
   };
 
   // ======================= schedule ==========================================
-  // Step s: state side of chunk s (A: P, O0; B: solve, update, output), the
-  // chunk-local matrices of chunk s (A, job waves) and the preparation of chunk
-  // s+1 (A: gate and norms, B: prefix, C: operands); three LDS-only barriers.
+  // Step s: the state side of chunk s (A: P, O0, decay, R; B: solve, update,
+  // output), the chunk-local matrices of chunk s (A) and the preparation of
+  // chunk s+1 (A: gate, prefix, value tile; B: norms and operands); two
+  // LDS-only barriers per step, the same count on every wave.
   if (nchunks > 0) {
-    // prologue: prepare chunk 0 into slot 0
-    load_raw(0);
-    prep_A(sm.slot[0], chunk_valid(0));
-    load_raw(nchunks > 1 ? 1 : 0);
-    lds_barrier();
-    prep_B(sm.slot[0]);
-    lds_barrier();
-    prep_C(sm.slot[0]);
-    lds_barrier();
-    for (int s = 0; s + 1 < nchunks; ++s) {
-      Slot<F>& cur = sm.slot[s & 1];
-      Slot<F>& nxt = sm.slot[(s + 1) & 1];
-      prep_A(nxt, chunk_valid(s + 1));
-      load_raw(s + 2 < nchunks ? s + 2 : nchunks - 1);
-      if (is_state) state_A(cur);
-      chunk_matrices(cur);
+    const int c1st = nchunks > 1 ? 1 : 0;
+    if constexpr (F::SPLIT) {
+      if (is_state) {
+        load_g(0);
+        load_qk(0);
+        gate(sm.slot[0], chunk_valid(0));
+        load_g(c1st);
+        lds_barrier();
+        prep_B(sm.slot[0]);
+        load_qk(c1st);
+        lds_barrier();
+        for (int s = 0; s < nchunks; ++s) {
+          Slot<F>& cur = sm.slot[s & 1];
+          Slot<F>& nxt = sm.slot[(s + 1) & 1];
+          const bool more = s + 1 < nchunks;  // uniform
+          const int nxt2 = s + 2 < nchunks ? s + 2 : nchunks - 1;
+          state_A(cur);
+          if (more) {
+            gate(nxt, chunk_valid(s + 1));
+            load_g(nxt2);
+          }
+          state_R(cur);
+          lds_barrier();
+          state_B(cur, s0 + (int64_t)s * C, chunk_valid(s));
+          if (more) {
+            prep_B(nxt);
+            load_qk(nxt2);
+          }
+          lds_barrier();
+        }
+      } else {
+        load_vb(0);
+        load_qk(0);
+        stage_vb(sm.slot[0], chunk_valid(0));
+        load_vb(c1st);
+        lds_barrier();
+        prep_B(sm.slot[0]);
+        load_qk(c1st);
+        lds_barrier();
+        for (int s = 0; s < nchunks; ++s) {
+          Slot<F>& cur = sm.slot[s & 1];
+          Slot<F>& nxt = sm.slot[(s + 1) & 1];
+          const bool more = s + 1 < nchunks;  // uniform
+          const int nxt2 = s + 2 < nchunks ? s + 2 : nchunks - 1;
+          if (more) {
+            stage_vb(nxt, chunk_valid(s + 1));
+            load_vb(nxt2);
+          }
+          chunk_matrices(cur);
+          lds_barrier();
+          if (more) {
+            prep_B(nxt);
+            load_qk(nxt2);
+          }
+          lds_barrier();
+        }
+      }
+    } else {
+      load_g(0);
+      load_vb(0);
+      load_qk(0);
+      gate(sm.slot[0], chunk_valid(0));
+      stage_vb(sm.slot[0], chunk_valid(0));
+      load_g(c1st);
+      load_vb(c1st);
       lds_barrier();
-      prep_B(nxt);
-      if (is_state) state_B(cur);
+      prep_B(sm.slot[0]);
+      load_qk(c1st);
       lds_barrier();
-      prep_C(nxt);
-      store_out(s0 + (int64_t)s * C, C);
-      lds_barrier();
-    }
-    // epilogue: the last chunk
-    {
-      const int s = nchunks - 1;
-      Slot<F>& cur = sm.slot[s & 1];
-      if (is_state) state_A(cur);
-      chunk_matrices(cur);
-      lds_barrier();
-      if (is_state) state_B(cur);
-      lds_barrier();
-      store_out(s0 + (int64_t)s * C, chunk_valid(s));
+      for (int s = 0; s < nchunks; ++s) {
+        Slot<F>& cur = sm.slot[s & 1];
+        Slot<F>& nxt = sm.slot[(s + 1) & 1];
+        const bool more = s + 1 < nchunks;  // uniform
+        const int nxt2 = s + 2 < nchunks ? s + 2 : nchunks - 1;
+        if (is_state) state_A(cur);
+        if (more) {
+          gate(nxt, chunk_valid(s + 1));
+          stage_vb(nxt, chunk_valid(s + 1));
+          load_g(nxt2);
+          load_vb(nxt2);
+        }
+        if (is_state) state_R(cur);
+        chunk_matrices(cur);
+        lds_barrier();
+        if (is_state) state_B(cur, s0 + (int64_t)s * C, chunk_valid(s));
+        if (more) {
+          prep_B(nxt);
+          load_qk(nxt2);
+        }
+        lds_barrier();
+      }
     }
   }
 
