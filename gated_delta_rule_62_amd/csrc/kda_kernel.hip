@@ -134,8 +134,15 @@ struct Cfg {
   static constexpr bool SPLIT = NW - NSW >= 4;
   static constexpr int JOB_BASE = SPLIT ? NSW : 0;
   static constexpr int NJW = NW - JOB_BASE;      // job waves (they also stage v and beta)
-  static constexpr int NGW = SPLIT ? NSW : NW;   // gate waves
-  static constexpr int EPT = C * D / NTHR;       // row layout (q, k; every wave): positions per thread
+  // gate waves: the job waves when there are eight of them (the state waves then
+  // only run the recurrence), else every wave
+  static constexpr bool GATE_ON_JOBS = SPLIT && NJW >= 8;
+  static constexpr int NGW = GATE_ON_JOBS ? NJW : NW;
+  // waves that prepare the exponent-scaled operands: every wave, or only the job
+  // waves when there are eight of them
+  static constexpr int NBW = (SPLIT && NJW >= 8) ? NJW : NW;
+  static constexpr int BBASE = NW - NBW;
+  static constexpr int EPT = C * D / (NBW * 64); // row layout (q, k): positions per thread
   static constexpr int TPR = D / EPT;            // threads per chunk row
   static constexpr int EPV = C * VT / (NJW * 64);  // value row layout (job waves): elements per thread
   static constexpr int TPRV = VT / EPV;          // threads per value row
@@ -344,6 +351,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   const bool is_job = wave >= F::JOB_BASE;     // uniform per wave
   const int jw = is_job ? wave - F::JOB_BASE : 0;        // index among the job waves
   const int jtid = is_job ? tid - F::JOB_BASE * 64 : 0;  // thread index among them
+  const bool is_bwave = wave >= F::BBASE;                   // prepares operands
+  const int btid = is_bwave ? tid - F::BBASE * 64 : 0;
 
   // ---- work item ---------------------------------------------------------
   const int vt_idx = blockIdx.x % p.n_vtiles;
@@ -368,16 +377,19 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     return rem < C ? (int)rem : C;
   };
 
-  // ---- state in: S^T accumulators of the state waves -------------------------
+  // ---- state: S^T accumulators of the state waves -----------------------------
+  // Loaded and stored only inside the state waves' code paths, so no other wave
+  // keeps registers for it.
   const int wv0 = wave * 16 * F::NTW;          // first value column of a state wave (in the tile)
   const int vbase = vt_idx * VT + wv0;         // ... in the head
   const int64_t sbase = ((int64_t)n * H + h) * D * D;
   f32x4_t S[F::KT][F::NTW];
+  auto state_in = [&]() {
 #pragma unroll
-  for (int kt = 0; kt < F::KT; ++kt)
+    for (int kt = 0; kt < F::KT; ++kt)
 #pragma unroll
-    for (int nt = 0; nt < F::NTW; ++nt) S[kt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (is_state && p.s_in != nullptr) {
+      for (int nt = 0; nt < F::NTW; ++nt) S[kt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (p.s_in == nullptr) return;
 #pragma unroll
     for (int kt = 0; kt < F::KT; ++kt)
 #pragma unroll
@@ -391,7 +403,23 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
           S[kt][nt] = f32x4_t{bflo(w[0]), bfhi(w[0]), bflo(w[1]), bfhi(w[1])};
         }
       }
-  }
+  };
+  auto state_out = [&]() {
+    if (p.s_out == nullptr) return;
+#pragma unroll
+    for (int kt = 0; kt < F::KT; ++kt)
+#pragma unroll
+      for (int nt = 0; nt < F::NTW; ++nt) {
+        const int64_t off = sbase + (int64_t)(vbase + 16 * nt + l16) * D + 16 * kt + 4 * lg;
+        const f32x4_t sv = S[kt][nt];
+        if (p.s_out_fp32) {
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.s_out) + off) = sv;
+        } else {
+          *reinterpret_cast<u32x2_t*>(static_cast<u16*>(p.s_out) + off) =
+              u32x2_t{pack_bf16(sv[0], sv[1]), pack_bf16(sv[2], sv[3])};
+        }
+      }
+  };
 
   // The block above the diagonal of Mqk is never written: zero it once.
   if constexpr (F::CT == 2) {
@@ -513,13 +541,14 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   // Column layout (g, gate, prefix; gate waves): pass ps covers key columns
   // g_col0 + 16 ps and g_col0 + 16 ps + 1 (lane bits 0-2 pick the pair) and chunk
   // rows g_row0 .. g_row0 + RPG - 1 (lane bits 3-5 pick one of eight row groups).
-  const int g_col0 = wave * F::SCOLS + 2 * (lane & 7);
+  const int gw = F::GATE_ON_JOBS ? jw : wave;  // index among the gate waves
+  const int g_col0 = gw * F::SCOLS + 2 * (lane & 7);
   const int g_rg = lane >> 3;
   const int g_row0 = g_rg * F::RPG;
-  // Row layout (q, k, operands; every wave): chunk row r_row, positions r_col ..
+  // Row layout (q, k, operands; operand waves): chunk row r_row, positions r_col ..
   // r_col + EPT - 1.
-  const int r_row = tid / F::TPR;
-  const int r_col = (tid % F::TPR) * F::EPT;
+  const int r_row = btid / F::TPR;
+  const int r_col = (btid % F::TPR) * F::EPT;
   // Value row layout (job waves).
   const int v_row = jtid / F::TPRV;
   const int v_col = (jtid % F::TPRV) * F::EPV;
@@ -781,17 +810,24 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   // output), the chunk-local matrices of chunk s (A) and the preparation of
   // chunk s+1 (A: gate, prefix, value tile; B: norms and operands); two
   // LDS-only barriers per step, the same count on every wave.
-  if (nchunks > 0) {
-    const int c1st = nchunks > 1 ? 1 : 0;
-    if constexpr (F::SPLIT) {
-      if (is_state) {
-        load_g(0);
-        load_qk(0);
-        gate(sm.slot[0], chunk_valid(0));
-        load_g(c1st);
+  const int c1st = nchunks > 1 ? 1 : 0;
+  if constexpr (F::SPLIT) {
+    if (is_state) {
+      constexpr bool ops = F::BBASE == 0;         // the state waves share the operands
+      constexpr bool gates = !F::GATE_ON_JOBS;    // ... and a share of the gate
+      state_in();
+      if (nchunks > 0) {
+        if (gates) load_g(0);
+        if (ops) load_qk(0);
+        if (gates) {
+          gate(sm.slot[0], chunk_valid(0));
+          load_g(c1st);
+        }
         lds_barrier();
-        prep_B(sm.slot[0]);
-        load_qk(c1st);
+        if (ops) {
+          prep_B(sm.slot[0]);
+          load_qk(c1st);
+        }
         lds_barrier();
         for (int s = 0; s < nchunks; ++s) {
           Slot<F>& cur = sm.slot[s & 1];
@@ -799,47 +835,57 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
           const bool more = s + 1 < nchunks;  // uniform
           const int nxt2 = s + 2 < nchunks ? s + 2 : nchunks - 1;
           state_A(cur);
-          if (more) {
+          if (gates && more) {
             gate(nxt, chunk_valid(s + 1));
             load_g(nxt2);
           }
           state_R(cur);
           lds_barrier();
           state_B(cur, s0 + (int64_t)s * C, chunk_valid(s));
-          if (more) {
-            prep_B(nxt);
-            load_qk(nxt2);
-          }
-          lds_barrier();
-        }
-      } else {
-        load_vb(0);
-        load_qk(0);
-        stage_vb(sm.slot[0], chunk_valid(0));
-        load_vb(c1st);
-        lds_barrier();
-        prep_B(sm.slot[0]);
-        load_qk(c1st);
-        lds_barrier();
-        for (int s = 0; s < nchunks; ++s) {
-          Slot<F>& cur = sm.slot[s & 1];
-          Slot<F>& nxt = sm.slot[(s + 1) & 1];
-          const bool more = s + 1 < nchunks;  // uniform
-          const int nxt2 = s + 2 < nchunks ? s + 2 : nchunks - 1;
-          if (more) {
-            stage_vb(nxt, chunk_valid(s + 1));
-            load_vb(nxt2);
-          }
-          chunk_matrices(cur);
-          lds_barrier();
-          if (more) {
+          if (ops && more) {
             prep_B(nxt);
             load_qk(nxt2);
           }
           lds_barrier();
         }
       }
-    } else {
+      state_out();
+    } else if (nchunks > 0) {
+      constexpr bool gates = true;  // every job wave takes a share of the gate
+      if (gates) load_g(0);
+      load_vb(0);
+      load_qk(0);
+      if (gates) gate(sm.slot[0], chunk_valid(0));
+      stage_vb(sm.slot[0], chunk_valid(0));
+      if (gates) load_g(c1st);
+      load_vb(c1st);
+      lds_barrier();
+      prep_B(sm.slot[0]);
+      load_qk(c1st);
+      lds_barrier();
+      for (int s = 0; s < nchunks; ++s) {
+        Slot<F>& cur = sm.slot[s & 1];
+        Slot<F>& nxt = sm.slot[(s + 1) & 1];
+        const bool more = s + 1 < nchunks;  // uniform
+        const int nxt2 = s + 2 < nchunks ? s + 2 : nchunks - 1;
+        if (more) {
+          if (gates) gate(nxt, chunk_valid(s + 1));
+          stage_vb(nxt, chunk_valid(s + 1));
+          if (gates) load_g(nxt2);
+          load_vb(nxt2);
+        }
+        chunk_matrices(cur);
+        lds_barrier();
+        if (more) {
+          prep_B(nxt);
+          load_qk(nxt2);
+        }
+        lds_barrier();
+      }
+    }
+  } else {
+    if (is_state) state_in();
+    if (nchunks > 0) {
       load_g(0);
       load_vb(0);
       load_qk(0);
@@ -874,23 +920,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
         lds_barrier();
       }
     }
-  }
-
-  // ---- state out ------------------------------------------------------------
-  if (is_state && p.s_out != nullptr) {
-#pragma unroll
-    for (int kt = 0; kt < F::KT; ++kt)
-#pragma unroll
-      for (int nt = 0; nt < F::NTW; ++nt) {
-        const int64_t off = sbase + (int64_t)(vbase + 16 * nt + l16) * D + 16 * kt + 4 * lg;
-        const f32x4_t sv = S[kt][nt];
-        if (p.s_out_fp32) {
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.s_out) + off) = sv;
-        } else {
-          *reinterpret_cast<u32x2_t*>(static_cast<u16*>(p.s_out) + off) =
-              u32x2_t{pack_bf16(sv[0], sv[1]), pack_bf16(sv[2], sv[3])};
-        }
-      }
+    if (is_state) state_out();
   }
 }
 
