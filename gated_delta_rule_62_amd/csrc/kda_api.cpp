@@ -11,9 +11,13 @@
 namespace {
 
 constexpr double kLog2e = 1.4426950408889634;
-// Largest |base-2 exponent| a centred bf16 operand may need: 2^126 keeps every
+// Largest base-2 exponent a centred bf16 operand may reach: 2^126 keeps every
 // scaled operand (|kh| <= 1, scale included) below the bf16 maximum.
-constexpr double kMaxRadius = 126.0;
+constexpr double kMaxExp = 126.0;
+// Largest anchor magnitude: the kernel's unscaled products Kc S^T and S Qc^T
+// reach 2^-Ca times a state row's 1-norm, and 2^110 leaves fp32 room for rows up
+// to 2^18.
+constexpr double kMaxAnchor = 110.0;
 
 struct Range {
   uintptr_t lo;
@@ -32,10 +36,16 @@ bool overlaps(Range a, Range b) {
   return a.lo < b.hi && b.lo < a.hi;
 }
 
-// Exponent radius (base 2) of the centred chunk operands: (chunk / 2) * |lb| * log2(e).
-double chunk_radius(double lb, int chunk) { return 0.5 * chunk * std::fabs(lb) * kLog2e; }
+// Decay span (base 2) of a chunk: the largest magnitude of its prefix, chunk |lb| log2(e).
+double chunk_span(double lb, int chunk) { return chunk * std::fabs(lb) * kLog2e; }
 
-int auto_chunk(double lb) { return chunk_radius(lb, 32) <= kMaxRadius ? 32 : 16; }
+// The anchor Ca = min(0, 126 - span) lies in the bf16-safe window [-126, 126 - span];
+// it is admissible when -Ca <= 110, i.e. span <= 236.
+bool chunk_admissible(double lb, int chunk) {
+  return chunk_span(lb, chunk) <= kMaxExp + kMaxAnchor;
+}
+
+int auto_chunk(double lb) { return chunk_admissible(lb, 32) ? 32 : 16; }
 
 int auto_v_tile(int64_t D) { return static_cast<int>(D); }
 
@@ -68,7 +78,7 @@ int resolve(const void* q, const void* k, const void* v, const void* g, const vo
   int chunk = chunk_size;
   if (chunk == 0) chunk = auto_chunk(lower_bound);
   if (chunk != 16 && chunk != 32) return KDA_ERR_BAD_SCHEDULE;
-  if (chunk_radius(lower_bound, chunk) > kMaxRadius) return KDA_ERR_BAD_LOWER_BOUND;
+  if (!chunk_admissible(lower_bound, chunk)) return KDA_ERR_BAD_LOWER_BOUND;
   int vt = v_tile == 0 ? auto_v_tile(D) : v_tile;
   if (!kda::kda_schedule_supported(static_cast<int>(D), chunk, vt)) return KDA_ERR_BAD_SCHEDULE;
 
@@ -165,7 +175,8 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
 }
 
 float kda_chunk_anchor(float lower_bound, int chunk_size) {
-  return static_cast<float>(0.5 * chunk_size * static_cast<double>(lower_bound) * kLog2e);
+  const double a = kMaxExp - chunk_span(lower_bound, chunk_size);
+  return static_cast<float>(a < 0.0 ? a : 0.0);
 }
 
 const char* kda_status_string(int status) {

@@ -11,8 +11,9 @@
 //   2. inclusive prefix G over the chunk per key column; a = 2^G_T
 //   3. operands (bf16, round to nearest even):
 //        centred  Qc = qh 2^(G-Ca), Kc = kh 2^(G-Ca), Ki = kh 2^(Ca-G)
-//        decayed  Qd = qh 2^G,      Kd = kh 2^G,      Kr = kh 2^(G_T-G)
-//      with the fixed anchor Ca = (C/2) lb log2(e) (section 2: 16 b for C = 32)
+//        decayed  Kr = kh 2^(G_T-G)
+//      with a fixed anchor Ca (section 2 centres 32-token chunks on 16 b; any
+//      anchor gives the same products, see below)
 //   4. L = strictLower(diag(beta) Kc Ki^T), Mqk = lowerTri(Qc Ki^T)  (bf16 MFMA,
 //      masked by select so overflowed upper entries never propagate)
 //   5. (I + L)^-1 in fp32 on the 16x16 diagonal blocks (forward substitution);
@@ -20,6 +21,16 @@
 //   6. state side, per wave on its own value columns (section 3):
 //        P^T = Kd S^T, O0 = S Qd^T, R^T = diag(beta)(V - P^T), U^T = (I+L)^-1 R^T,
 //        S^T <- diag(a) S^T + Kr^T U^T,  O = O0 + U Mqk^T
+//      where the decayed operands Qd = qh 2^G = 2^Ca Qc and Kd = 2^Ca Kc are
+//      never formed: P^T = 2^Ca (Kc S^T) and O = 2^Ca (S Qc^T + U (2^-Ca Mqk)^T),
+//      the power of two applied to the fp32 results.
+//
+// Anchor.  The centred operands stay inside the bf16 range when
+// -126 <= Ca <= 126 + C b (b = lb log2(e), so C b bounds the prefix of a chunk).
+// The library takes the top of that interval, Ca = min(0, 126 + C b): Ki then
+// reaches at most 2^126 and Kc, Qc at most 2^-Ca, which keeps the unscaled
+// products Kc S^T and S Qc^T far from the fp32 range (the host limits -Ca to
+// 110, so state rows up to 2^18 in 1-norm are safe).
 //
 // Schedule.  Steps 1-5 only touch chunk-local data, step 6 is the strictly
 // ordered recurrence (section 3's scheduling property).  Waves 0..NSW-1 hold the
@@ -45,7 +56,7 @@
 // and the operands read from LDS use the same permutation, so the product is
 // exact whatever order the hardware reduces in.  The A and B operands of the
 // MFMA share one lane layout, so the same packed registers serve either side:
-// P^T = Kd S^T takes S^T as B, O0 = S Qd^T takes it as A, which leaves O with
+// P^T = Kc S^T takes S^T as B, O0 = S Qc^T takes it as A, which leaves O with
 // four consecutive values of one token in each lane, ready for an 8-byte store.
 // The q/k-side operands are stored with their key columns already in pi order
 // (position 8g + i holds key 4g + i, position 8g + 4 + i holds key 16 + 4g + i
@@ -181,8 +192,6 @@ __device__ constexpr int job_wave(int j) {
 // Prepared operands of one chunk.
 template <class F>
 struct alignas(16) Slot {
-  u16 Qd[F::C][F::LDQ];      // pi-ordered key positions
-  u16 Kd[F::C][F::LDQ];      // pi-ordered key positions
   u16 Kr[F::C][F::LDR];      // natural key order (read transposed)
   u16 SOL[F::C][F::LDC];     // [[X11, 0], [-L21, X22]]: X = (I + L)^-1 diagonal blocks
   u16 Mqk[F::C][F::LDC];
@@ -194,7 +203,8 @@ struct alignas(16) Slot {
 template <class F>
 struct alignas(16) Smem {
   Slot<F> slot[2];
-  u16 Qc[F::C][F::LDQ];      // centred operands of the chunk being prepared (pi order)
+  u16 Qc[F::C][F::LDQ];      // centred operands (pi order) of the chunk whose state side,
+                             // matrices and preparation alternate in them
   u16 Kc[F::C][F::LDQ];
   u16 Ki[F::C][F::LDQ];
   float G[F::C][F::LDG];     // inclusive base-2 decay prefix of the chunk being prepared
@@ -372,6 +382,9 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   const int64_t H = p.H;
   const int nchunks = (int)((s1 - s0 + C - 1) / C);
   const uint32_t row_bytes = (uint32_t)(H * D * 2);
+  const float Ca = p.anchor;
+  const float c1 = __builtin_amdgcn_exp2f(Ca);    // 2^Ca
+  const float c1i = __builtin_amdgcn_exp2f(-Ca);  // 2^-Ca
   auto chunk_valid = [&](int c) -> int {
     const int64_t rem = s1 - (s0 + (int64_t)c * C);
     return rem < C ? (int)rem : C;
@@ -431,7 +444,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
 
   // ======================= state side (state waves) ==========================
   f32x4_t P[F::CT][F::NTW], O[F::CT][F::NTW];
-  // A: P^T = Kd S^T and O0 = S Qd^T with the decay S^T <- diag(a) S^T alongside
+  // A: P'^T = Kc S^T and O0' = S Qc^T (P = 2^Ca P', O0 = 2^Ca O0') with the decay
+  // S^T <- diag(a) S^T alongside
   // (state_A), then R^T = diag(beta)(V - P^T) in place in P (state_R).
   auto state_A = [&](Slot<F>& cur) {
 #pragma unroll
@@ -458,8 +472,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       }
 #pragma unroll
       for (int ct = 0; ct < F::CT; ++ct) {
-        const u32x4_t aK = lds_op_pi(&cur.Kd[16 * ct + l16][0], 32 * ks, lg);
-        const u32x4_t aQ = lds_op_pi(&cur.Qd[16 * ct + l16][0], 32 * ks, lg);
+        const u32x4_t aK = lds_op_pi(&sm.Kc[16 * ct + l16][0], 32 * ks, lg);
+        const u32x4_t aQ = lds_op_pi(&sm.Qc[16 * ct + l16][0], 32 * ks, lg);
 #pragma unroll
         for (int nt = 0; nt < F::NTW; ++nt) {
           P[ct][nt] = mfma_k32(aK, bS[nt], P[ct][nt]);
@@ -476,10 +490,10 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       for (int nt = 0; nt < F::NTW; ++nt) {
         // lane: value column wv0 + 16 nt + l16, chunk rows 16 ct + 4 lg .. +3
         const u32x2_t vv = lds_col4<F::LDV>(&cur.V[16 * ct][0], wv0 + 16 * nt, l16, lg);
-        P[ct][nt][0] = b4[0] * (bflo(vv[0]) - P[ct][nt][0]);
-        P[ct][nt][1] = b4[1] * (bfhi(vv[0]) - P[ct][nt][1]);
-        P[ct][nt][2] = b4[2] * (bflo(vv[1]) - P[ct][nt][2]);
-        P[ct][nt][3] = b4[3] * (bfhi(vv[1]) - P[ct][nt][3]);
+        P[ct][nt][0] = b4[0] * __builtin_fmaf(-c1, P[ct][nt][0], bflo(vv[0]));
+        P[ct][nt][1] = b4[1] * __builtin_fmaf(-c1, P[ct][nt][1], bfhi(vv[0]));
+        P[ct][nt][2] = b4[2] * __builtin_fmaf(-c1, P[ct][nt][2], bflo(vv[1]));
+        P[ct][nt][3] = b4[3] * __builtin_fmaf(-c1, P[ct][nt][3], bfhi(vv[1]));
       }
     }
   };
@@ -517,7 +531,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) S[kt][nt] = mfma_k32(aR, bU[nt], S[kt][nt]);
     }
-    // O = O0 + U Mqk^T: U as the A operand (value rows), Mqk rows as B (token columns)
+    // O = 2^Ca (O0' + U Mqk'^T), Mqk' = 2^-Ca Mqk: U as the A operand (value rows),
+    // Mqk' rows as B (token columns)
     const __amdgpu_buffer_rsrc_t ro =
         make_rsrc(p.out + (cur_start * H + h) * D + vt_idx * VT, cur_valid * (int)row_bytes);
 #pragma unroll
@@ -527,7 +542,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       else bM = lds_op_pad(&cur.Mqk[l16][0], lg);
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) {
-        const f32x4_t o = mfma_k32(bU[nt], bM, O[ct][nt]);
+        const f32x4_t o = c1 * mfma_k32(bU[nt], bM, O[ct][nt]);
         // lane: token 16 ct + l16, values wv0 + 16 nt + 4 lg .. +3
         const u32x2_t w = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
         __builtin_amdgcn_raw_buffer_store_b64(
@@ -560,8 +575,6 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
 #pragma unroll
     for (int c = 0; c < 2; ++c)
       gate_add[ps][c] = gate_mul * p.dt_bias[(int64_t)h * D + g_col0 + 16 * ps + c];
-  const float Ca = p.anchor;
-  const float c1 = __builtin_amdgcn_exp2f(Ca);  // 2^Ca
 
   // Raw inputs of the chunk to prepare next, in registers.  Buffer loads through a
   // descriptor bounded to the chunk's valid rows: rows past the end of the
@@ -691,7 +704,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     constexpr int RUN = F::EPT < 8 ? F::EPT : 8;
 #pragma unroll
     for (int r0 = 0; r0 < F::EPT; r0 += RUN) {
-      float oQc[RUN], oKc[RUN], oKi[RUN], oQd[RUN], oKd[RUN], oKr[RUN];
+      float oQc[RUN], oKc[RUN], oKi[RUN], oKr[RUN];
 #pragma unroll
       for (int j = 0; j < RUN / 4; ++j) {
         const int key = pi_key(r_col + r0 + 4 * j);
@@ -704,12 +717,9 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
           const float d = gg[e] - Ca;
           const float e1 = __builtin_amdgcn_exp2f(d);   // 2^(G - Ca)
           const float e2 = __builtin_amdgcn_exp2f(-d);  // 2^(Ca - G)
-          const float ed = e1 * c1;                     // 2^G
           oQc[x] = qv * e1;
           oKc[x] = kv * e1;
           oKi[x] = kv * e2;
-          oQd[x] = qv * ed;
-          oKd[x] = kv * ed;
           oKr[x] = oKi[x] * tt[e];                      // kh 2^(G_T - G)
         }
         store_bf16<4>(&nxt.Kr[r_row][key], &oKr[4 * j]);
@@ -717,8 +727,6 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       store_bf16<RUN>(&sm.Qc[r_row][r_col + r0], oQc);
       store_bf16<RUN>(&sm.Kc[r_row][r_col + r0], oKc);
       store_bf16<RUN>(&sm.Ki[r_row][r_col + r0], oKi);
-      store_bf16<RUN>(&nxt.Qd[r_row][r_col + r0], oQd);
-      store_bf16<RUN>(&nxt.Kd[r_row][r_col + r0], oKd);
     }
   };
   // A: the chunk-local matrices of the current chunk from its centred operands,
@@ -738,7 +746,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int i = 16 * ti + 4 * lg + ii;
-        cur.Mqk[i][j] = to_bf16((j <= i) ? acc[ii] : 0.f);
+        cur.Mqk[i][j] = to_bf16((j <= i) ? acc[ii] * c1i : 0.f);  // stored as 2^-Ca Mqk
       }
       return;
     }

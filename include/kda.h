@@ -17,6 +17,9 @@
  * with qh, kh the L2-normalised q and k rows (x / sqrt(|x|^2 + 1e-6)).  The
  * library evaluates this in chunks of 16 or 32 tokens with bf16 matrix-core
  * products and an fp32 state that stays on chip for the whole sequence.
+ * Within a chunk the decayed operands are centred on a fixed exponent anchor
+ * (section 2 of the PR #4262 summary); the state rows' 1-norms must stay below
+ * 2^18 for the centred state products to stay inside fp32.
  *
  * Conventions for every entry point:
  *   - Every pointer argument except `stream` is a caller-owned DEVICE pointer
@@ -48,8 +51,8 @@ extern "C" {
                                      /* num_seqs != B without cu_seqlens                 */
 #define KDA_ERR_BAD_ALIAS (-5)       /* an output overlaps an input or the other output; */
                                      /* only the exact in-place state alias is allowed   */
-#define KDA_ERR_BAD_LOWER_BOUND (-6) /* lower_bound not finite, not < 0, or beyond the   */
-                                     /* bf16 exponent-safe radius of the chunk size      */
+#define KDA_ERR_BAD_LOWER_BOUND (-6) /* lower_bound not finite, not < 0, or too strong   */
+                                     /* for the chunk size (see kda_fwd)                 */
 #define KDA_ERR_BAD_SCALE (-7)       /* scale not finite                                 */
 #define KDA_ERR_BAD_SCHEDULE (-8)    /* unsupported forced chunk size or value tile      */
 #define KDA_ERR_HIP (-9)             /* the HIP runtime reported an error at launch      */
@@ -91,10 +94,10 @@ extern "C" {
  *   B, T, H, D     sizes; D in {32, 64, 128}.
  *   stream         a hipStream_t (NULL: the null stream).
  *
- * Returns KDA_OK or a negative status.  lower_bound must satisfy
- * |lower_bound| * log2(e) * 8 <= 126 (|lb| <= 10.92); the library uses 32-token
- * chunks when |lb| * log2(e) * 16 <= 126 (|lb| <= 5.458) and 16-token chunks
- * otherwise, each centred on the fixed anchor (chunk/2) * lb * log2(e).
+ * Returns KDA_OK or a negative status.  The decay span of a chunk is
+ * chunk * |lower_bound| * log2(e); it must not exceed 236 (|lb| <= 10.22 with
+ * 16-token chunks).  The library uses 32-token chunks when their span allows it
+ * (|lb| <= 5.112) and 16-token chunks otherwise; see kda_chunk_anchor.
  */
 int kda_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
             float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
@@ -105,7 +108,7 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
 /*
  * kda_fwd_sched -- kda_fwd with a forced schedule, for tests and tuning.
  *   chunk_size  0 (automatic), 16 or 32.  32 is rejected (KDA_ERR_BAD_LOWER_BOUND)
- *               when |lb| > 5.458.
+ *               when |lb| > 5.112.
  *   v_tile      0 (automatic) or the number of value rows one workgroup owns:
  *               a divisor of D that is a multiple of 16 and at least 32
  *               (KDA_ERR_BAD_SCHEDULE otherwise).
@@ -132,10 +135,15 @@ int kda_fwd_check(const void* q, const void* k, const void* v, const void* g, co
                   int v_tile);
 
 /*
- * kda_chunk_anchor -- the fixed exponent anchor (base 2) used for a chunk size:
- * (chunk_size / 2) * lower_bound * log2(e).  For 32-token chunks this is the
- * anchor 16 * lower_bound * log2(e) of section 2 of the PR #4262 summary
- * (about -115.42 for lower_bound = -5).  Pure host function.
+ * kda_chunk_anchor -- the fixed exponent anchor Ca (base 2) the library centres a
+ * chunk's operands on: min(0, 126 - chunk_size * |lower_bound| * log2(e)).
+ * Section 2 of the PR #4262 summary centres on the middle of the window,
+ * 16 * lower_bound * log2(e) for 32-token chunks (about -115.42 for
+ * lower_bound = -5); every anchor in [-126, 126 - span] keeps the centred
+ * operands inside the bf16 range and gives the same products, and the library
+ * takes the top of that window (about -104.83 for lower_bound = -5), which keeps
+ * the operands it also uses for the state products as small as possible.
+ * Pure host function.
  */
 float kda_chunk_anchor(float lower_bound, int chunk_size);
 

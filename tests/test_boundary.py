@@ -3,7 +3,6 @@ host-side validation returns the documented status codes (no GPU call is made:
 kda_fwd_check only compares pointer values and sizes)."""
 from __future__ import annotations
 
-import json
 import math
 import os
 import re
@@ -47,12 +46,20 @@ def test_status_strings(lib):
     assert "UNKNOWN" in kda.kda_status_string(-1234)
 
 
-def test_anchor_matches_printed_value(lib):
-    with open(os.path.join(ROOT, "tests", "golden", "anchor_constants.json")) as f:
-        gold = json.load(f)
-    a = kda.kda_chunk_anchor(gold["lower_bound"], gold["chunk"])
-    assert round(a, gold["anchor_decimals"]) == gold["anchor_printed"]
-    assert abs(kda.kda_chunk_anchor(-5.0, 16) - a / 2) < 1e-4
+def test_anchor_window(lib):
+    """The library anchor sits at the top of the bf16-safe window [-126, 126 - span]
+    (span = chunk |lb| log2 e) and never needs more than 2^110 of headroom."""
+    log2e = 1.4426950408889634
+    for lb in (-0.01, -0.5, -1.0, -3.0, -5.0, -5.1):
+        for chunk in (16, 32):
+            span = chunk * abs(lb) * log2e
+            a = kda.kda_chunk_anchor(lb, chunk)
+            assert abs(a - min(0.0, 126.0 - span)) < 1e-4, (lb, chunk, a)
+            assert -126.0 <= a <= 126.0 - span + 1e-4
+            assert -a <= 110.0 + 1e-4
+    # lb = -5, 32-token chunks: 126 - 32 * 5 * log2(e) = -104.83
+    assert abs(kda.kda_chunk_anchor(-5.0, 32) + 104.8312) < 1e-3
+    assert kda.kda_chunk_anchor(-5.0, 16) == 0.0
 
 
 # fake device addresses, far apart so that only deliberate overlaps overlap
@@ -110,13 +117,13 @@ def test_scalar_errors(lib):
     for lb in (0.0, 1.0, float("nan"), float("inf"), float("-inf")):
         assert _check(lb=lb) == kda.KDA_ERR_BAD_LOWER_BOUND, lb
     assert _check(scale=float("nan")) == kda.KDA_ERR_BAD_SCALE
-    # exponent-safe radius: 32-token chunks to |lb| = 126 / (16 log2 e) = 5.458...,
-    # 16-token chunks to 10.91...; the automatic schedule falls back to 16.
-    assert _check(lb=-5.45, chunk=32) == kda.KDA_OK
-    assert _check(lb=-5.47, chunk=32) == kda.KDA_ERR_BAD_LOWER_BOUND
-    assert _check(lb=-5.47) == kda.KDA_OK
-    assert _check(lb=-10.9) == kda.KDA_OK
-    assert _check(lb=-10.95) == kda.KDA_ERR_BAD_LOWER_BOUND
+    # decay span chunk |lb| log2(e) <= 236: 32-token chunks to |lb| = 5.1118,
+    # 16-token chunks to 10.2236; the automatic schedule falls back to 16.
+    assert _check(lb=-5.11, chunk=32) == kda.KDA_OK
+    assert _check(lb=-5.12, chunk=32) == kda.KDA_ERR_BAD_LOWER_BOUND
+    assert _check(lb=-5.12) == kda.KDA_OK
+    assert _check(lb=-10.22) == kda.KDA_OK
+    assert _check(lb=-10.23) == kda.KDA_ERR_BAD_LOWER_BOUND
 
 
 def test_schedule_errors(lib):
