@@ -150,11 +150,19 @@ def test_large_state_magnitude():
     # fp32 results by a power of two; the unscaled products grow with the state's row
     # norms.  A fp32 state ~ N(0, 40^2) (row 1-norms near 4e3) and values scaled by
     # 50 keep every row well inside the documented 2^18 bound.
+    # The absolute max-abs bound is scaled with the data (rel-L2 is scale-free).
     w = Workload("bigstate", B=1, T=200, H=2, D=128, seed=16, state_in="fp32", state_out="fp32")
     inp = make_inputs(w, device=DEV)
     inp["initial_state"].mul_(400.0)
     inp["v"].mul_(50.0)
-    _check_against_oracle(inp, tag="large state")
+    _run(inp)
+    out_ref, fin_ref = _oracle(inp)
+    for what, x, ref in (("large state out", inp["out"], out_ref),
+                         ("large state final_state", inp["final_state"], fin_ref)):
+        mx, rel = _errors(x, ref)
+        peak = float(np.abs(ref).max())
+        print("%s: max-abs %.3e (peak %.3e) rel-L2 %.3e" % (what, mx, peak, rel), flush=True)
+        assert mx <= MAX_ABS * peak and rel <= REL_L2, what
 
 
 def test_projection_property_on_gpu():
