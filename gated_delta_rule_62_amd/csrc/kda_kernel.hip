@@ -49,23 +49,24 @@
 //
 // Layout of the state in registers.  Each wave holds S^T (K rows x its value
 // columns) as 16x16 fp32 accumulator tiles: lane l owns value column (l & 15)
-// and key rows 4*(l >> 4) + i, i < 4.  An accumulator tile pair (key rows
-// 32s..32s+31) becomes a bf16 operand of a 16x16x32 MFMA directly: lane group
-// g = l >> 4 then carries the reduction indices
-//   pi_g = {32s + 4g + i} U {32s + 16 + 4g + i},  i < 4,
-// and the operands read from LDS use the same permutation, so the product is
-// exact whatever order the hardware reduces in.  The A and B operands of the
-// MFMA share one lane layout, so the same packed registers serve either side:
-// P^T = Kc S^T takes S^T as B, O0 = S Qc^T takes it as A, which leaves O with
-// four consecutive values of one token in each lane, ready for an 8-byte store.
-// The q/k-side operands are stored with their key columns already in pi order
-// (position 8g + i holds key 4g + i, position 8g + 4 + i holds key 16 + 4g + i
-// inside each 32-column block), so each operand is one 16-byte LDS read.  The
-// same holds for the C-long reductions (U, the state update and the output)
-// with the chunk tiles; with 16-token chunks the upper four slots of both
-// operands are zero.  Every bf16 product uses the one 16x16x32 shape: a
-// 16x16x16 MFMA that accumulates onto a 16x16x32 result was observed to read
-// part of that accumulator before the first instruction had written it.
+// and rows 4*(l >> 4) + i, i < 4.  The rows are the keys in a fixed order:
+// inside each 32-row block, row 4g + i holds key 8g + i and row 16 + 4g + i holds
+// key 8g + 4 + i (sigma below).  An accumulator tile pair (rows 32s..32s+31)
+// then becomes a bf16 operand of a 16x16x32 MFMA directly, and lane group g
+// carries the eight consecutive keys 32s + 8g .. 32s + 8g + 7 as its reduction
+// slots, which is exactly a 16-byte read of a key-ordered LDS row.  So the
+// q/k-side operands stay in natural key order (one 16-byte global load, one
+// 16-byte LDS read per operand); only the state's load and store, the decay
+// vector and the Kr tile (whose columns the state update reads as rows) follow
+// the row order.  The A and B operands of the MFMA share one lane layout, so the
+// same packed registers serve either side: P^T = Kc S^T takes S^T as B,
+// O0 = S Qc^T takes it as A, which leaves O with four consecutive values of one
+// token in each lane, ready for an 8-byte store.  The C-long reductions (U, the
+// state update and the output) use the token analogue of the same slot order;
+// with 16-token chunks the upper four slots of both operands are zero.  Every
+// bf16 product uses the one 16x16x32 shape: a 16x16x16 MFMA that accumulates
+// onto a 16x16x32 result was observed to read part of that accumulator before
+// the first instruction had written it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -119,9 +120,12 @@ __device__ __forceinline__ float fast_sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
 }
 
-// Key column held at position p of a pi-ordered row (see the header comment).
-__host__ __device__ constexpr int pi_key(int p) {
-  return (p & ~31) + (((p & 31) >> 3) << 2) + ((p & 4) ? 16 : 0) + (p & 3);
+// Key held by state row r (sigma in the header comment), and the row of key k.
+__host__ __device__ constexpr int key_of_row(int r) {
+  return (r & ~31) + (((r & 15) >> 2) << 3) + ((r & 16) ? 4 : 0) + (r & 3);
+}
+__host__ __device__ constexpr int row_of_key(int k) {
+  return (k & ~31) + (((k & 31) >> 3) << 2) + ((k & 4) ? 16 : 0) + (k & 3);
 }
 
 template <int D_, int C_, int VT_, int NW_, int NSW_>
@@ -192,18 +196,18 @@ __device__ constexpr int job_wave(int j) {
 // Prepared operands of one chunk.
 template <class F>
 struct alignas(16) Slot {
-  u16 Kr[F::C][F::LDR];      // natural key order (read transposed)
+  u16 Kr[F::C][F::LDR];      // columns in state-row order (read transposed)
   u16 SOL[F::C][F::LDC];     // [[X11, 0], [-L21, X22]]: X = (I + L)^-1 diagonal blocks
   u16 Mqk[F::C][F::LDC];
   u16 V[F::C][F::LDV];
-  float a[2 * F::D];         // 2^G_T (second half: discarded writes)
+  float a[2 * F::D];         // 2^G_T in state-row order (second half: discarded writes)
   float beta[F::C];          // sigmoid(beta), zero past the sequence
 };
 
 template <class F>
 struct alignas(16) Smem {
   Slot<F> slot[2];
-  u16 Qc[F::C][F::LDQ];      // centred operands (pi order) of the chunk whose state side,
+  u16 Qc[F::C][F::LDQ];      // centred operands (key order) of the chunk whose state side,
                              // matrices and preparation alternate in them
   u16 Kc[F::C][F::LDQ];
   u16 Ki[F::C][F::LDQ];
@@ -233,9 +237,9 @@ __device__ __forceinline__ void store_bf16(u16* p, const float* x) {
   store_words<N>(p, w);
 }
 
-// Operand (16 rows x 32 reductions) of a 16x16x32 MFMA from a pi-ordered bf16 LDS
-// row: row r, positions k0 + 8g .. k0 + 8g + 7.
-__device__ __forceinline__ u32x4_t lds_op_pi(const u16* row, int k0, int g) {
+// Operand (16 rows x 32 reductions) of a 16x16x32 MFMA from a key-ordered bf16 LDS
+// row: row r, columns k0 + 8g .. k0 + 8g + 7 (the reduction slots of lane group g).
+__device__ __forceinline__ u32x4_t lds_op_k(const u16* row, int k0, int g) {
   return *reinterpret_cast<const u32x4_t*>(row + k0 + 8 * g);
 }
 // Operand from a naturally ordered [C][C] bf16 row with the pi_g permutation:
@@ -407,7 +411,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     for (int kt = 0; kt < F::KT; ++kt)
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) {
-        const int64_t off = sbase + (int64_t)(vbase + 16 * nt + l16) * D + 16 * kt + 4 * lg;
+        const int64_t off =
+            sbase + (int64_t)(vbase + 16 * nt + l16) * D + key_of_row(16 * kt + 4 * lg);
         if (p.s_in_fp32) {
           S[kt][nt] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.s_in) + off);
         } else {
@@ -423,7 +428,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     for (int kt = 0; kt < F::KT; ++kt)
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) {
-        const int64_t off = sbase + (int64_t)(vbase + 16 * nt + l16) * D + 16 * kt + 4 * lg;
+        const int64_t off =
+            sbase + (int64_t)(vbase + 16 * nt + l16) * D + key_of_row(16 * kt + 4 * lg);
         const f32x4_t sv = S[kt][nt];
         if (p.s_out_fp32) {
           *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.s_out) + off) = sv;
@@ -472,8 +478,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       }
 #pragma unroll
       for (int ct = 0; ct < F::CT; ++ct) {
-        const u32x4_t aK = lds_op_pi(&sm.Kc[16 * ct + l16][0], 32 * ks, lg);
-        const u32x4_t aQ = lds_op_pi(&sm.Qc[16 * ct + l16][0], 32 * ks, lg);
+        const u32x4_t aK = lds_op_k(&sm.Kc[16 * ct + l16][0], 32 * ks, lg);
+        const u32x4_t aQ = lds_op_k(&sm.Qc[16 * ct + l16][0], 32 * ks, lg);
 #pragma unroll
         for (int nt = 0; nt < F::NTW; ++nt) {
           P[ct][nt] = mfma_k32(aK, bS[nt], P[ct][nt]);
@@ -580,12 +586,11 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   // descriptor bounded to the chunk's valid rows: rows past the end of the
   // sequence read as zero, without branches.  Offsets are 32-bit (the host bounds
   // C * H * D * 2 below 2^31).
-  const uint32_t off_qk = (uint32_t)r_row * row_bytes;
+  const uint32_t off_qk = (uint32_t)r_row * row_bytes + (uint32_t)r_col * 2;
   const uint32_t off_v = (uint32_t)v_row * row_bytes + (uint32_t)(vt_idx * VT + v_col) * 2;
   const uint32_t off_g = (uint32_t)g_row0 * row_bytes + (uint32_t)g_col0 * 2;
   const uint32_t off_b = (uint32_t)jtid * (uint32_t)(H * 2);
-  constexpr int NP = F::EPT / 4;  // 4-key pieces per thread in the row layout
-  u32x2_t raw_q[NP], raw_k[NP];
+  unsigned raw_q[F::EPT / 2], raw_k[F::EPT / 2];
   unsigned raw_v[F::EPV / 2];
   unsigned raw_g[F::SPASS][F::RPG];
   unsigned raw_b = 0;
@@ -613,14 +618,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     const int64_t cs = s0 + (int64_t)c * C;
     const int64_t tok_elem = (cs * H + h) * D;
     const int nb = chunk_valid(c) * (int)row_bytes;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + tok_elem, nb);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + tok_elem, nb);
-#pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      const uint32_t o = off_qk + (uint32_t)pi_key(r_col + 4 * j) * 2;
-      raw_q[j] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rq, o, 0, 0));
-      raw_k[j] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rk, o, 0, 0));
-    }
+    buf_load<F::EPT>(make_rsrc(p.q + tok_elem, nb), off_qk, raw_q);
+    buf_load<F::EPT>(make_rsrc(p.k + tok_elem, nb), off_qk, raw_k);
   };
   // Exclusive prefix over the eight row groups (lanes c, c+8, ..., c+56) of a
   // per-lane total t.  Row groups 2r and 2r+1 share the 16-lane row r: a DPP
@@ -665,12 +664,14 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       for (int i = 0; i < F::RPG; ++i)
         *reinterpret_cast<f32x2_t*>(&sm.G[g_row0 + i][col]) = f32x2_t{run0[i] + off0, run1[i] + off1};
       // G_T is the last row, held by row group 7; the other groups write the same
-      // expressions into a discarded half of each array (no branch).
+      // expressions into a discarded half of each array (no branch).  The decay
+      // vector a goes to the state's row order (col is even, so the pair stays
+      // adjacent), 2^(G_T - Ca) stays in key order.
       const float gt0 = t0 + off0, gt1 = t1 + off1;
-      const int dst = (g_rg == 7) ? col : F::D + col;
-      *reinterpret_cast<f32x2_t*>(&nxt.a[dst]) =
+      const int discard = (g_rg == 7) ? 0 : F::D;
+      *reinterpret_cast<f32x2_t*>(&nxt.a[discard + row_of_key(col)]) =
           f32x2_t{__builtin_amdgcn_exp2f(gt0), __builtin_amdgcn_exp2f(gt1)};
-      *reinterpret_cast<f32x2_t*>(&sm.gtc[dst]) =
+      *reinterpret_cast<f32x2_t*>(&sm.gtc[discard + col]) =
           f32x2_t{__builtin_amdgcn_exp2f(gt0 - Ca), __builtin_amdgcn_exp2f(gt1 - Ca)};
     }
   };
@@ -679,22 +680,17 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     store_words<F::EPV>(&nxt.V[v_row][v_col], raw_v);
     if (jtid < C) nxt.beta[jtid] = jtid < nxt_valid ? fast_sigmoid(bf2f((u16)raw_b)) : 0.f;
   };
-  // B: norms and exponent-scaled operands of the next chunk.  Position 4j + e of
-  // this thread's run holds key pi_key(r_col + 4j) + e.
+  // B: norms and exponent-scaled operands of the next chunk (keys r_col ..
+  // r_col + EPT - 1 of chunk row r_row).
   auto prep_B = [&](Slot<F>& nxt) {
     float qn[F::EPT], kn[F::EPT];
     float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      qn[4 * j] = bflo(raw_q[j][0]); qn[4 * j + 1] = bfhi(raw_q[j][0]);
-      qn[4 * j + 2] = bflo(raw_q[j][1]); qn[4 * j + 3] = bfhi(raw_q[j][1]);
-      kn[4 * j] = bflo(raw_k[j][0]); kn[4 * j + 1] = bfhi(raw_k[j][0]);
-      kn[4 * j + 2] = bflo(raw_k[j][1]); kn[4 * j + 3] = bfhi(raw_k[j][1]);
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        sq = dot2_bf16(raw_q[j][w], raw_q[j][w], sq);
-        sk = dot2_bf16(raw_k[j][w], raw_k[j][w], sk);
-      }
+    for (int w = 0; w < F::EPT / 2; ++w) {
+      qn[2 * w] = bflo(raw_q[w]); qn[2 * w + 1] = bfhi(raw_q[w]);
+      kn[2 * w] = bflo(raw_k[w]); kn[2 * w + 1] = bfhi(raw_k[w]);
+      sq = dot2_bf16(raw_q[w], raw_q[w], sq);
+      sk = dot2_bf16(raw_k[w], raw_k[w], sk);
     }
     sq = group_sum<F::TPR>(sq);
     sk = group_sum<F::TPR>(sk);
@@ -707,7 +703,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       float oQc[RUN], oKc[RUN], oKi[RUN], oKr[RUN];
 #pragma unroll
       for (int j = 0; j < RUN / 4; ++j) {
-        const int key = pi_key(r_col + r0 + 4 * j);
+        const int key = r_col + r0 + 4 * j;
         const f32x4_t gg = *reinterpret_cast<const f32x4_t*>(&sm.G[r_row][key]);
         const f32x4_t tt = *reinterpret_cast<const f32x4_t*>(&sm.gtc[key]);
 #pragma unroll
@@ -722,7 +718,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
           oKi[x] = kv * e2;
           oKr[x] = oKi[x] * tt[e];                      // kh 2^(G_T - G)
         }
-        store_bf16<4>(&nxt.Kr[r_row][key], &oKr[4 * j]);
+        store_bf16<4>(&nxt.Kr[r_row][row_of_key(key)], &oKr[4 * j]);
       }
       store_bf16<RUN>(&sm.Qc[r_row][r_col + r0], oQc);
       store_bf16<RUN>(&sm.Kc[r_row][r_col + r0], oKc);
@@ -740,7 +736,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     const u16* brow = &sm.Ki[16 * tj + l16][0];
 #pragma unroll
     for (int ks = 0; ks < F::KS; ++ks)
-      acc = mfma_k32(lds_op_pi(arow, 32 * ks, lg), lds_op_pi(brow, 32 * ks, lg), acc);
+      acc = mfma_k32(lds_op_k(arow, 32 * ks, lg), lds_op_k(brow, 32 * ks, lg), acc);
     const int j = 16 * tj + l16;
     if (!is_l) {
 #pragma unroll
@@ -947,7 +943,7 @@ hipError_t launch_one(const KdaParams& p, hipStream_t stream) {
 #define KDA_SCHEDULES(X)  \
   X(128, 32, 128, 8, 4)   \
   X(128, 16, 128, 8, 4)   \
-  X(128, 32, 64, 4, 4)    \
+  X(128, 32, 64, 8, 4)    \
   X(128, 16, 64, 4, 4)    \
   X(64, 32, 64, 4, 4)     \
   X(64, 16, 64, 4, 4)     \
