@@ -47,7 +47,24 @@ bool chunk_admissible(double lb, int chunk) {
 
 int auto_chunk(double lb) { return chunk_admissible(lb, 32) ? 32 : 16; }
 
-int auto_v_tile(int64_t D) { return static_cast<int>(D); }
+// Compute units of the current device (256 on MI355X when the query fails, e.g.
+// without a GPU).
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;
+  return cus;
+}
+
+// One workgroup owns all value rows of a (sequence, head) unless there are so few
+// units that halving the value tile still leaves one workgroup per compute unit:
+// the halves repeat the chunk preparation but split the state work.
+int auto_v_tile(int64_t D, int chunk, int64_t units) {
+  if (D == 128 && chunk == 32 && 2 * units <= device_cus()) return 64;
+  return static_cast<int>(D);
+}
 
 int resolve(const void* q, const void* k, const void* v, const void* g, const void* beta,
             float scale, const void* out, const float* A_log, const float* dt_bias,
@@ -79,7 +96,7 @@ int resolve(const void* q, const void* k, const void* v, const void* g, const vo
   if (chunk == 0) chunk = auto_chunk(lower_bound);
   if (chunk != 16 && chunk != 32) return KDA_ERR_BAD_SCHEDULE;
   if (!chunk_admissible(lower_bound, chunk)) return KDA_ERR_BAD_LOWER_BOUND;
-  int vt = v_tile == 0 ? auto_v_tile(D) : v_tile;
+  int vt = v_tile == 0 ? auto_v_tile(D, chunk, num_seqs * H) : v_tile;
   if (!kda::kda_schedule_supported(static_cast<int>(D), chunk, vt)) return KDA_ERR_BAD_SCHEDULE;
 
   // Buffer extents and the aliasing contract.

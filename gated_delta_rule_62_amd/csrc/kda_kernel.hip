@@ -454,13 +454,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   // S^T <- diag(a) S^T alongside
   // (state_A), then R^T = diag(beta)(V - P^T) in place in P (state_R).
   auto state_A = [&](Slot<F>& cur) {
-#pragma unroll
-    for (int ct = 0; ct < F::CT; ++ct)
-#pragma unroll
-      for (int nt = 0; nt < F::NTW; ++nt) {
-        P[ct][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        O[ct][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
     // one 32-row key step at a time: its bf16 copy of S^T is live only there, and
     // once it is taken the decay of those rows proceeds while the products run
 #pragma unroll
@@ -482,8 +476,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
         const u32x4_t aQ = lds_op_k(&sm.Qc[16 * ct + l16][0], 32 * ks, lg);
 #pragma unroll
         for (int nt = 0; nt < F::NTW; ++nt) {
-          P[ct][nt] = mfma_k32(aK, bS[nt], P[ct][nt]);
-          O[ct][nt] = mfma_k32(bS[nt], aQ, O[ct][nt]);
+          P[ct][nt] = mfma_k32(aK, bS[nt], ks == 0 ? zero : P[ct][nt]);
+          O[ct][nt] = mfma_k32(bS[nt], aQ, ks == 0 ? zero : O[ct][nt]);
         }
       }
     }

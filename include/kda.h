@@ -111,7 +111,10 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
  *               when |lb| > 5.112.
  *   v_tile      0 (automatic) or the number of value rows one workgroup owns:
  *               a divisor of D that is a multiple of 16 and at least 32
- *               (KDA_ERR_BAD_SCHEDULE otherwise).
+ *               (KDA_ERR_BAD_SCHEDULE otherwise).  Automatic: D, or D/2 for
+ *               D = 128 with 32-token chunks when twice num_seqs * H workgroups
+ *               still fit one per compute unit of the current device (queried
+ *               on the host; the host never synchronises).
  * Everything else is exactly as kda_fwd.
  */
 int kda_fwd_sched(const void* q, const void* k, const void* v, const void* g, const void* beta,
