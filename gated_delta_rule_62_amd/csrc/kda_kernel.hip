@@ -141,18 +141,15 @@ struct Cfg {
   static constexpr int CT = C / 16;            // 16-row chunk tiles
   static constexpr int NTW = VT / (16 * NSW);  // 16-column value tiles per state wave
   // Role split: with at least four waves beyond the state waves, the state waves
-  // also compute the gate and its prefix while the other waves (job waves) run
-  // the chunk-local matrix jobs and stage the value tile; every wave takes a share
-  // of the exponent-scaled operands.  The two roles run separate loops with the
-  // same barriers.  With fewer waves every wave takes a share of everything in
-  // one loop.
+  // also compute the whole gate and its prefix while the other waves (job waves)
+  // run the chunk-local matrix jobs and stage the value tile; every wave takes a
+  // share of the exponent-scaled operands.  The two roles run separate loops with
+  // the same barriers.  With fewer waves every wave takes a share of everything
+  // in one loop.
   static constexpr bool SPLIT = NW - NSW >= 4;
   static constexpr int JOB_BASE = SPLIT ? NSW : 0;
   static constexpr int NJW = NW - JOB_BASE;      // job waves (they also stage v and beta)
-  // gate waves: the job waves when there are eight of them (the state waves then
-  // only run the recurrence), else every wave
-  static constexpr bool GATE_ON_JOBS = SPLIT && NJW >= 8;
-  static constexpr int NGW = GATE_ON_JOBS ? NJW : NW;
+  static constexpr int NGW = SPLIT ? NSW : NW;   // gate waves: the state waves in the split
   // waves that prepare the exponent-scaled operands: every wave, or only the job
   // waves when there are eight of them
   static constexpr int NBW = (SPLIT && NJW >= 8) ? NJW : NW;
@@ -556,7 +553,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   // Column layout (g, gate, prefix; gate waves): pass ps covers key columns
   // g_col0 + 16 ps and g_col0 + 16 ps + 1 (lane bits 0-2 pick the pair) and chunk
   // rows g_row0 .. g_row0 + RPG - 1 (lane bits 3-5 pick one of eight row groups).
-  const int gw = F::GATE_ON_JOBS ? jw : wave;  // index among the gate waves
+  const int gw = (F::SPLIT && !is_state) ? 0 : wave;  // index among the gate waves
   const int g_col0 = gw * F::SCOLS + 2 * (lane & 7);
   const int g_rg = lane >> 3;
   const int g_row0 = g_rg * F::RPG;
@@ -812,15 +809,12 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   if constexpr (F::SPLIT) {
     if (is_state) {
       constexpr bool ops = F::BBASE == 0;         // the state waves share the operands
-      constexpr bool gates = !F::GATE_ON_JOBS;    // ... and a share of the gate
       state_in();
       if (nchunks > 0) {
-        if (gates) load_g(0);
+        load_g(0);
         if (ops) load_qk(0);
-        if (gates) {
-          gate(sm.slot[0], chunk_valid(0));
-          load_g(c1st);
-        }
+        gate(sm.slot[0], chunk_valid(0));
+        load_g(c1st);
         lds_barrier();
         if (ops) {
           prep_B(sm.slot[0]);
@@ -833,7 +827,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
           const bool more = s + 1 < nchunks;  // uniform
           const int nxt2 = s + 2 < nchunks ? s + 2 : nchunks - 1;
           state_A(cur);
-          if (gates && more) {
+          if (more) {
             gate(nxt, chunk_valid(s + 1));
             load_g(nxt2);
           }
@@ -849,13 +843,9 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       }
       state_out();
     } else if (nchunks > 0) {
-      constexpr bool gates = true;  // every job wave takes a share of the gate
-      if (gates) load_g(0);
       load_vb(0);
       load_qk(0);
-      if (gates) gate(sm.slot[0], chunk_valid(0));
       stage_vb(sm.slot[0], chunk_valid(0));
-      if (gates) load_g(c1st);
       load_vb(c1st);
       lds_barrier();
       prep_B(sm.slot[0]);
@@ -867,9 +857,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
         const bool more = s + 1 < nchunks;  // uniform
         const int nxt2 = s + 2 < nchunks ? s + 2 : nchunks - 1;
         if (more) {
-          if (gates) gate(nxt, chunk_valid(s + 1));
           stage_vb(nxt, chunk_valid(s + 1));
-          if (gates) load_g(nxt2);
           load_vb(nxt2);
         }
         chunk_matrices(cur);
