@@ -109,8 +109,8 @@ def cpu_baseline(inp, min_wall: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="batched")
     ap.add_argument("--chunk", type=int, default=None, help="force the chunk size")
     ap.add_argument("--v-tile", type=int, default=0, help="force the value tile")
