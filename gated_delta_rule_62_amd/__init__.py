@@ -13,8 +13,8 @@ import os
 
 from ._build import LIB_PATH, build  # noqa: F401  (build() is the in-tree compile step)
 
-__all__ = ["kda_fwd", "kda_fwd_sched", "kda_fwd_check", "kda_chunk_anchor",
-           "kda_status_string", "KdaError", "library_path", "load_library"]
+__all__ = ["kda_fwd", "kda_fwd_sched", "kda_fwd_ordered", "kda_longest_first", "kda_fwd_check",
+           "kda_chunk_anchor", "kda_status_string", "KdaError", "library_path", "load_library"]
 
 KDA_OK = 0
 KDA_ERR_NULL_ARG = -1
@@ -60,6 +60,10 @@ def load_library():
     lib.kda_fwd.restype = i32
     lib.kda_fwd_sched.argtypes = common + [vp, i32, i32]
     lib.kda_fwd_sched.restype = i32
+    lib.kda_fwd_ordered.argtypes = common + [vp, vp]
+    lib.kda_fwd_ordered.restype = i32
+    lib.kda_longest_first.argtypes = [vp, i64, vp, vp]
+    lib.kda_longest_first.restype = i32
     lib.kda_fwd_check.argtypes = common + [i32, i32]
     lib.kda_fwd_check.restype = i32
     lib.kda_chunk_anchor.argtypes = [f32, i32]
@@ -92,18 +96,10 @@ def _state_dtype_code(t):
     raise TypeError("state tensors must be bfloat16 or float32, got %s" % t.dtype)
 
 
-def kda_fwd_sched(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
-                  initial_state=None, final_state=None, cu_seqlens=None,
-                  chunk_size: int = 0, v_tile: int = 0, stream=None) -> None:
-    """Runs the forward on the device tensors given (asynchronous on ``stream``).
-
-    q, k, v, g, out: bf16 ``[B,T,H,D]``; beta bf16 ``[B,T,H]``; A_log fp32 ``[H]``;
-    dt_bias fp32 ``[H,D]``; states ``[N,H,D,D]`` bf16 or fp32 (or None);
-    cu_seqlens int64 ``[N+1]`` on the device (varlen, B == 1) or None (batched).
-    ``stream`` defaults to torch's current stream on q's device.
-    """
+def _marshal(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+             final_state, cu_seqlens, stream, extra=()):
+    """Checks the tensors and returns the C arguments shared by every forward entry point."""
     import torch
-    lib = load_library()
     acts = {"q": q, "k": k, "v": v, "g": g, "out": out}
     for name, t in acts.items():
         if t.dtype != torch.bfloat16 or t.dim() != 4:
@@ -124,7 +120,7 @@ def kda_fwd_sched(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
         N = cu_seqlens.numel() - 1
     else:
         N = B
-    tensors = [q, k, v, g, beta, out, A_log, dt_bias]
+    tensors = [q, k, v, g, beta, out, A_log, dt_bias] + list(extra)
     for t in (initial_state, final_state, cu_seqlens):
         if t is not None:
             tensors.append(t)
@@ -141,14 +137,69 @@ def kda_fwd_sched(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
         stream = torch.cuda.current_stream(dev)
     s_ptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     ptr = lambda t: None if t is None else t.data_ptr()
-    st = lib.kda_fwd_sched(
-        ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), float(scale), ptr(out), ptr(A_log),
-        ptr(dt_bias), float(lower_bound), ptr(initial_state),
-        _state_dtype_code(initial_state) if initial_state is not None else 0, ptr(final_state),
-        _state_dtype_code(final_state) if final_state is not None else 0, ptr(cu_seqlens), N, B,
-        T, H, D, s_ptr, int(chunk_size), int(v_tile))
+    return (ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), float(scale), ptr(out), ptr(A_log),
+            ptr(dt_bias), float(lower_bound), ptr(initial_state),
+            _state_dtype_code(initial_state) if initial_state is not None else 0,
+            ptr(final_state), _state_dtype_code(final_state) if final_state is not None else 0,
+            ptr(cu_seqlens), N, B, T, H, D, s_ptr)
+
+
+def kda_fwd_sched(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                  initial_state=None, final_state=None, cu_seqlens=None,
+                  chunk_size: int = 0, v_tile: int = 0, stream=None) -> None:
+    """Runs the forward on the device tensors given (asynchronous on ``stream``).
+
+    q, k, v, g, out: bf16 ``[B,T,H,D]``; beta bf16 ``[B,T,H]``; A_log fp32 ``[H]``;
+    dt_bias fp32 ``[H,D]``; states ``[N,H,D,D]`` bf16 or fp32 (or None);
+    cu_seqlens int64 ``[N+1]`` on the device (varlen, B == 1) or None (batched).
+    ``stream`` defaults to torch's current stream on q's device.
+    """
+    args = _marshal(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                    final_state, cu_seqlens, stream)
+    st = load_library().kda_fwd_sched(*args, int(chunk_size), int(v_tile))
     if st != KDA_OK:
         raise KdaError(st)
+
+
+def kda_fwd_ordered(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, seq_order,
+                    initial_state=None, final_state=None, cu_seqlens=None, stream=None) -> None:
+    """``kda_fwd`` with the workgroups of sequence ``seq_order[0]`` dispatched first, then
+    ``seq_order[1]``, ...  ``seq_order``: int32 ``[N]`` device permutation (see
+    ``kda_longest_first``).  The results are bitwise those of ``kda_fwd``."""
+    import torch
+    if seq_order.dtype != torch.int32 or seq_order.dim() != 1:
+        raise ValueError("seq_order must be a 1-d int32 tensor")
+    args = _marshal(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                    final_state, cu_seqlens, stream, extra=(seq_order,))
+    if seq_order.numel() != args[15]:
+        raise ValueError("seq_order must have one entry per sequence")
+    st = load_library().kda_fwd_ordered(*args, seq_order.data_ptr())
+    if st != KDA_OK:
+        raise KdaError(st)
+
+
+def kda_longest_first(cu_seqlens, seq_order=None, stream=None):
+    """Longest-first order (int32 ``[N]``, on the device) of the sequences of ``cu_seqlens``,
+    computed by the library's ordering kernel; written into ``seq_order`` if given."""
+    import torch
+    if cu_seqlens.dtype != torch.int64 or cu_seqlens.dim() != 1 or not cu_seqlens.is_cuda:
+        raise ValueError("cu_seqlens must be a 1-d int64 GPU tensor")
+    if not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be contiguous")
+    N = cu_seqlens.numel() - 1
+    if seq_order is None:
+        seq_order = torch.empty(max(N, 0), dtype=torch.int32, device=cu_seqlens.device)
+    elif (seq_order.dtype != torch.int32 or tuple(seq_order.shape) != (N,)
+          or seq_order.device != cu_seqlens.device or not seq_order.is_contiguous()):
+        raise ValueError("seq_order must be a contiguous int32 [N] tensor on cu_seqlens' GPU")
+    if stream is None:
+        stream = torch.cuda.current_stream(cu_seqlens.device)
+    s_ptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = load_library().kda_longest_first(cu_seqlens.data_ptr(), N, seq_order.data_ptr()
+                                          if N > 0 else None, s_ptr)
+    if st != KDA_OK:
+        raise KdaError(st)
+    return seq_order
 
 
 def kda_fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None,

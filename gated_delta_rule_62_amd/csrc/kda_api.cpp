@@ -71,7 +71,7 @@ int resolve(const void* q, const void* k, const void* v, const void* g, const vo
             float lower_bound, const void* initial_state, int initial_state_dtype,
             const void* final_state, int final_state_dtype, const int64_t* cu_seqlens,
             int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t D, int chunk_size,
-            int v_tile, int* chunk_out, int* v_tile_out) {
+            int v_tile, const int32_t* seq_order, int* chunk_out, int* v_tile_out) {
   if (!q || !k || !v || !g || !beta || !out || !A_log || !dt_bias) return KDA_ERR_NULL_ARG;
   if (B < 1 || H < 1 || T < 0) return KDA_ERR_BAD_SHAPE;
   if (T == 0 && cu_seqlens == nullptr) return KDA_ERR_BAD_SHAPE;
@@ -107,12 +107,13 @@ int resolve(const void* q, const void* k, const void* v, const void* g, const vo
               rg = make_range(g, act), rb = make_range(beta, tok * H * 2),
               ra = make_range(A_log, H * 4), rd = make_range(dt_bias, H * D * 4),
               rc = make_range(cu_seqlens, cu_seqlens ? (num_seqs + 1) * 8 : 0),
+              ro = make_range(seq_order, seq_order ? num_seqs * 4 : 0),
               rs_in = make_range(initial_state,
                                  initial_state ? st_elems * (initial_state_dtype ? 4 : 2) : 0),
               rout = make_range(out, act),
               rs_out = make_range(final_state,
                                   final_state ? st_elems * (final_state_dtype ? 4 : 2) : 0);
-  const Range inputs_but_state[] = {rq, rk, rv, rg, rb, ra, rd, rc};
+  const Range inputs_but_state[] = {rq, rk, rv, rg, rb, ra, rd, rc, ro};
   for (const Range& r : inputs_but_state) {
     if (overlaps(rout, r) || overlaps(rs_out, r)) return KDA_ERR_BAD_ALIAS;
   }
@@ -124,6 +125,48 @@ int resolve(const void* q, const void* k, const void* v, const void* g, const vo
   *chunk_out = chunk;
   *v_tile_out = vt;
   return KDA_OK;
+}
+
+// Validates, fills the launch parameters and enqueues the kernel.
+int launch(const void* q, const void* k, const void* v, const void* g, const void* beta,
+           float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
+           const void* initial_state, int initial_state_dtype, void* final_state,
+           int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B,
+           int64_t T, int64_t H, int64_t D, void* stream, int chunk_size, int v_tile,
+           const int32_t* seq_order) {
+  int chunk = 0, vt = 0;
+  const int st = resolve(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                         initial_state, initial_state_dtype, final_state, final_state_dtype,
+                         cu_seqlens, num_seqs, B, T, H, D, chunk_size, v_tile, seq_order, &chunk,
+                         &vt);
+  if (st != KDA_OK) return st;
+
+  kda::KdaParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.g = static_cast<const uint16_t*>(g);
+  p.beta = static_cast<const uint16_t*>(beta);
+  p.out = static_cast<uint16_t*>(out);
+  p.A_log = A_log;
+  p.dt_bias = dt_bias;
+  p.s_in = initial_state;
+  p.s_out = final_state;
+  p.cu = cu_seqlens;
+  p.order = seq_order;
+  p.T = T;
+  p.T_total = B * T;
+  p.N = static_cast<int32_t>(num_seqs);
+  p.H = static_cast<int32_t>(H);
+  p.s_in_fp32 = initial_state_dtype == KDA_DTYPE_FP32 ? 1 : 0;
+  p.s_out_fp32 = final_state_dtype == KDA_DTYPE_FP32 ? 1 : 0;
+  p.n_vtiles = static_cast<int32_t>(D / vt);
+  p.scale = scale;
+  p.lb2 = static_cast<float>(lower_bound * kLog2e);
+  p.anchor = kda_chunk_anchor(lower_bound, chunk);
+  const hipError_t e =
+      kda::launch_kda_fwd(p, static_cast<int>(D), chunk, vt, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // namespace
@@ -139,7 +182,7 @@ int kda_fwd_check(const void* q, const void* k, const void* v, const void* g, co
   int c = 0, vt = 0;
   return resolve(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                  initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T,
-                 H, D, chunk_size, v_tile, &c, &vt);
+                 H, D, chunk_size, v_tile, nullptr, &c, &vt);
 }
 
 int kda_fwd_sched(const void* q, const void* k, const void* v, const void* g, const void* beta,
@@ -148,36 +191,32 @@ int kda_fwd_sched(const void* q, const void* k, const void* v, const void* g, co
                   void* final_state, int final_state_dtype, const int64_t* cu_seqlens,
                   int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t D, void* stream,
                   int chunk_size, int v_tile) {
-  int chunk = 0, vt = 0;
-  const int st = resolve(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
-                         initial_state, initial_state_dtype, final_state, final_state_dtype,
-                         cu_seqlens, num_seqs, B, T, H, D, chunk_size, v_tile, &chunk, &vt);
-  if (st != KDA_OK) return st;
+  return launch(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T,
+                H, D, stream, chunk_size, v_tile, nullptr);
+}
 
-  kda::KdaParams p;
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
-  p.g = static_cast<const uint16_t*>(g);
-  p.beta = static_cast<const uint16_t*>(beta);
-  p.out = static_cast<uint16_t*>(out);
-  p.A_log = A_log;
-  p.dt_bias = dt_bias;
-  p.s_in = initial_state;
-  p.s_out = final_state;
-  p.cu = cu_seqlens;
-  p.T = T;
-  p.T_total = B * T;
-  p.N = static_cast<int32_t>(num_seqs);
-  p.H = static_cast<int32_t>(H);
-  p.s_in_fp32 = initial_state_dtype == KDA_DTYPE_FP32 ? 1 : 0;
-  p.s_out_fp32 = final_state_dtype == KDA_DTYPE_FP32 ? 1 : 0;
-  p.n_vtiles = static_cast<int32_t>(D / vt);
-  p.scale = scale;
-  p.lb2 = static_cast<float>(lower_bound * kLog2e);
-  p.anchor = kda_chunk_anchor(lower_bound, chunk);
-  const hipError_t e =
-      kda::launch_kda_fwd(p, static_cast<int>(D), chunk, vt, static_cast<hipStream_t>(stream));
+int kda_fwd_ordered(const void* q, const void* k, const void* v, const void* g,
+                    const void* beta, float scale, void* out, const float* A_log,
+                    const float* dt_bias, float lower_bound, const void* initial_state,
+                    int initial_state_dtype, void* final_state, int final_state_dtype,
+                    const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H,
+                    int64_t D, void* stream, const int32_t* seq_order) {
+  if (!seq_order) return KDA_ERR_NULL_ARG;
+  return launch(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T,
+                H, D, stream, 0, 0, seq_order);
+}
+
+int kda_longest_first(const int64_t* cu_seqlens, int64_t num_seqs, int32_t* seq_order,
+                      void* stream) {
+  if (!cu_seqlens || !seq_order) return KDA_ERR_NULL_ARG;
+  if (num_seqs < 1 || num_seqs > kda::kMaxOrderSeqs) return KDA_ERR_BAD_VARLEN;
+  const Range rc = make_range(cu_seqlens, (num_seqs + 1) * 8);
+  const Range ro = make_range(seq_order, num_seqs * 4);
+  if (overlaps(rc, ro)) return KDA_ERR_BAD_ALIAS;
+  const hipError_t e = kda::launch_longest_first(cu_seqlens, static_cast<int>(num_seqs), seq_order,
+                                                 static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -369,7 +369,14 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   const int vt_idx = blockIdx.x % p.n_vtiles;
   const int unit = blockIdx.x / p.n_vtiles;
   const int h = unit % p.H;
-  const int n = unit / p.H;
+  // Workgroups are dispatched in index order, so a caller's sequence order (for
+  // example longest first) decides which sequences start first; it never changes
+  // what a workgroup computes.  Entries are clamped into [0, N).
+  int n = unit / p.H;
+  if (p.order != nullptr) {
+    const int o = p.order[n];
+    n = o < 0 ? 0 : (o >= p.N ? p.N - 1 : o);
+  }
   int64_t s0, s1;
   if (p.cu != nullptr) {
     s0 = p.cu[n];
@@ -933,6 +940,55 @@ hipError_t launch_one(const KdaParams& p, hipStream_t stream) {
   X(64, 16, 32, 2, 2)     \
   X(32, 32, 32, 2, 2)     \
   X(32, 16, 32, 2, 2)
+
+// Longest-first order of the sequences of a packed batch: one workgroup sorts the
+// keys (kMaxInt - length) << 32 | index ascending with a bitonic network in LDS,
+// so the longest sequence comes first and equal lengths keep their index order.
+namespace {
+constexpr int kOrderThreads = 1024;
+__global__ __launch_bounds__(kOrderThreads) void kda_order_kernel(const int64_t* cu, int num_seqs,
+                                                                   int padded, int32_t* order) {
+  __shared__ uint64_t key[kMaxOrderSeqs];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < padded; i += kOrderThreads) {
+    uint64_t kv = ~0ull;  // padding sorts last
+    if (i < num_seqs) {
+      int64_t len = cu[i + 1] - cu[i];
+      len = len < 0 ? 0 : (len > 0x7fffffff ? 0x7fffffff : len);
+      kv = ((uint64_t)(0x7fffffff - len) << 32) | (uint32_t)i;
+    }
+    key[i] = kv;
+  }
+  __syncthreads();
+  for (int size = 2; size <= padded; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < padded; i += kOrderThreads) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const uint64_t a = key[i], b = key[j];
+          const bool ascending = (i & size) == 0;
+          if ((a > b) == ascending) {
+            key[i] = b;
+            key[j] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < num_seqs; i += kOrderThreads) order[i] = (int32_t)(key[i] & 0xffffffffu);
+}
+}  // namespace
+
+hipError_t launch_longest_first(const int64_t* cu, int num_seqs, int32_t* order,
+                                hipStream_t stream) {
+  if (num_seqs < 1 || num_seqs > kMaxOrderSeqs) return hipErrorInvalidValue;
+  int padded = 1;
+  while (padded < num_seqs) padded <<= 1;
+  hipLaunchKernelGGL(kda_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, cu, num_seqs,
+                     padded, order);
+  return hipGetLastError();
+}
 
 bool kda_schedule_supported(int D, int chunk, int v_tile) {
 #define KDA_SUPPORTED(d, c, vt, nw, nsw) \

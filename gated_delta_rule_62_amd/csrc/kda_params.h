@@ -19,6 +19,7 @@ struct KdaParams {
   const void* s_in;         // [N, H, D, D] bf16/fp32 or nullptr
   void* s_out;              // [N, H, D, D] bf16/fp32 or nullptr
   const int64_t* cu;        // [N+1] or nullptr (batched)
+  const int32_t* order;     // [N] sequence order of the workgroups, or nullptr (identity)
   int64_t T;                // tokens per batch row (batched mode)
   int64_t T_total;          // B*T
   int32_t N;                // sequences
@@ -36,6 +37,14 @@ hipError_t launch_kda_fwd(const KdaParams& p, int D, int chunk, int v_tile, hipS
 
 // Whether a (D, chunk, v_tile) schedule has a compiled kernel.
 bool kda_schedule_supported(int D, int chunk, int v_tile);
+
+// Largest num_seqs the on-device longest-first ordering handles (one workgroup
+// sorts all lengths in LDS).
+constexpr int kMaxOrderSeqs = 8192;
+
+// Launches the longest-first ordering of num_seqs (<= kMaxOrderSeqs) sequences.
+hipError_t launch_longest_first(const int64_t* cu, int num_seqs, int32_t* order,
+                                hipStream_t stream);
 
 }  // namespace kda
 

@@ -125,6 +125,44 @@ int kda_fwd_sched(const void* q, const void* k, const void* v, const void* g, co
                   int chunk_size, int v_tile);
 
 /*
+ * kda_fwd_ordered -- kda_fwd with a caller-chosen order of the sequences over
+ * the workgroups (the sequence-order option of the FlashInfer PR #4262
+ * summary's integration section, where it serves tail utilisation).
+ *   seq_order  int32 [num_seqs] device array, a permutation of 0 .. num_seqs-1:
+ *              the workgroups of sequence seq_order[0] are dispatched first,
+ *              then those of seq_order[1], and so on.  Longest first (see
+ *              kda_longest_first) keeps long sequences of a packed batch from
+ *              starting last.  It must not overlap any output
+ *              (KDA_ERR_BAD_ALIAS); NULL is KDA_ERR_NULL_ARG.
+ * The results are bitwise those of kda_fwd: the order only changes which
+ * workgroup starts when.  The host never reads seq_order; entries outside
+ * [0, num_seqs) are clamped (in bounds, but the results are then unspecified).
+ * Everything else is exactly as kda_fwd.
+ */
+int kda_fwd_ordered(const void* q, const void* k, const void* v, const void* g,
+                    const void* beta, float scale, void* out, const float* A_log,
+                    const float* dt_bias, float lower_bound, const void* initial_state,
+                    int initial_state_dtype, void* final_state, int final_state_dtype,
+                    const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H,
+                    int64_t D, void* stream, const int32_t* seq_order);
+
+/*
+ * kda_longest_first -- writes the longest-first order of a packed batch for
+ * kda_fwd_ordered: seq_order[i] is the index of the sequence with the i-th
+ * largest length cu_seqlens[n+1] - cu_seqlens[n] (equal lengths keep their
+ * index order).  One small kernel on `stream`; the host reads nothing.
+ *   cu_seqlens  int64 [num_seqs + 1] device array (as for kda_fwd).
+ *   num_seqs    1 .. 8192 (KDA_ERR_BAD_VARLEN otherwise).
+ *   seq_order   int32 [num_seqs] device array, written; must not overlap
+ *               cu_seqlens (KDA_ERR_BAD_ALIAS).
+ * Returns KDA_OK, KDA_ERR_NULL_ARG, KDA_ERR_BAD_VARLEN, KDA_ERR_BAD_ALIAS or
+ * KDA_ERR_HIP.  An order depends only on the lengths, so one computation can
+ * serve every layer of a model that shares the batch.
+ */
+int kda_longest_first(const int64_t* cu_seqlens, int64_t num_seqs, int32_t* seq_order,
+                      void* stream);
+
+/*
  * kda_fwd_check -- the host-side validation of kda_fwd_sched on its own: the
  * same arguments without the stream, returns the status kda_fwd_sched would
  * return before launching.  Pure host code (pointer values are compared, never

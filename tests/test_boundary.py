@@ -150,3 +150,24 @@ def test_alias_contract(lib):
     # adjacent, non-overlapping buffers are fine: q ends where k starts
     act = 2 * 64 * 4 * 128 * 2
     assert _check(k=1 * GB + act) == kda.KDA_OK
+
+
+def _ordered(seq_order, **kw):
+    a = _args(**kw)
+    return kda.load_library().kda_fwd_ordered(*a[:-2], None, seq_order)
+
+
+def test_ordered_and_longest_first_validation(lib):
+    """Error paths of kda_fwd_ordered and kda_longest_first return before any launch."""
+    assert _ordered(None) == kda.KDA_ERR_NULL_ARG
+    # the order array is an input: no output may overlap it
+    assert _ordered(12 * GB, out=12 * GB) == kda.KDA_ERR_BAD_ALIAS
+    assert _ordered(12 * GB, B=1, T=100, N=2, has_cu=True, s_out=12 * GB) == kda.KDA_ERR_BAD_ALIAS
+    # everything kda_fwd rejects is still rejected
+    assert _ordered(12 * GB, lb=1.0) == kda.KDA_ERR_BAD_LOWER_BOUND
+    lf = lib.kda_longest_first
+    assert lf(None, 3, 12 * GB, None) == kda.KDA_ERR_NULL_ARG
+    assert lf(11 * GB, 3, None, None) == kda.KDA_ERR_NULL_ARG
+    assert lf(11 * GB, 0, 12 * GB, None) == kda.KDA_ERR_BAD_VARLEN
+    assert lf(11 * GB, 8193, 12 * GB, None) == kda.KDA_ERR_BAD_VARLEN
+    assert lf(11 * GB, 4, 11 * GB + 8, None) == kda.KDA_ERR_BAD_ALIAS
