@@ -13,7 +13,8 @@ import os
 
 from ._build import LIB_PATH, build  # noqa: F401  (build() is the in-tree compile step)
 
-__all__ = ["kda_fwd", "kda_fwd_sched", "kda_fwd_ordered", "kda_longest_first", "kda_fwd_check",
+__all__ = ["kda_fwd", "kda_fwd_sched", "kda_fwd_ordered", "kda_fwd_transposed_state",
+           "kda_longest_first", "kda_fwd_check",
            "kda_chunk_anchor", "kda_status_string", "KdaError", "library_path", "load_library"]
 
 KDA_OK = 0
@@ -62,6 +63,8 @@ def load_library():
     lib.kda_fwd_sched.restype = i32
     lib.kda_fwd_ordered.argtypes = common + [vp, vp]
     lib.kda_fwd_ordered.restype = i32
+    lib.kda_fwd_transposed_state.argtypes = common + [vp]
+    lib.kda_fwd_transposed_state.restype = i32
     lib.kda_longest_first.argtypes = [vp, i64, vp, vp]
     lib.kda_longest_first.restype = i32
     lib.kda_fwd_check.argtypes = common + [i32, i32]
@@ -174,6 +177,17 @@ def kda_fwd_ordered(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, s
     if seq_order.numel() != args[15]:
         raise ValueError("seq_order must have one entry per sequence")
     st = load_library().kda_fwd_ordered(*args, seq_order.data_ptr())
+    if st != KDA_OK:
+        raise KdaError(st)
+
+
+def kda_fwd_transposed_state(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                             initial_state=None, final_state=None, cu_seqlens=None,
+                             stream=None) -> None:
+    """``kda_fwd`` with both states in the key-major layout ``[N,H,D(k),D(v)]``."""
+    args = _marshal(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                    final_state, cu_seqlens, stream)
+    st = load_library().kda_fwd_transposed_state(*args)
     if st != KDA_OK:
         raise KdaError(st)
 

@@ -133,7 +133,7 @@ int launch(const void* q, const void* k, const void* v, const void* g, const voi
            const void* initial_state, int initial_state_dtype, void* final_state,
            int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B,
            int64_t T, int64_t H, int64_t D, void* stream, int chunk_size, int v_tile,
-           const int32_t* seq_order) {
+           const int32_t* seq_order, int state_kv) {
   int chunk = 0, vt = 0;
   const int st = resolve(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
                          initial_state, initial_state_dtype, final_state, final_state_dtype,
@@ -160,6 +160,7 @@ int launch(const void* q, const void* k, const void* v, const void* g, const voi
   p.H = static_cast<int32_t>(H);
   p.s_in_fp32 = initial_state_dtype == KDA_DTYPE_FP32 ? 1 : 0;
   p.s_out_fp32 = final_state_dtype == KDA_DTYPE_FP32 ? 1 : 0;
+  p.s_kv = state_kv;
   p.n_vtiles = static_cast<int32_t>(D / vt);
   p.scale = scale;
   p.lb2 = static_cast<float>(lower_bound * kLog2e);
@@ -193,7 +194,7 @@ int kda_fwd_sched(const void* q, const void* k, const void* v, const void* g, co
                   int chunk_size, int v_tile) {
   return launch(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                 initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T,
-                H, D, stream, chunk_size, v_tile, nullptr);
+                H, D, stream, chunk_size, v_tile, nullptr, 0);
 }
 
 int kda_fwd_ordered(const void* q, const void* k, const void* v, const void* g,
@@ -205,7 +206,18 @@ int kda_fwd_ordered(const void* q, const void* k, const void* v, const void* g,
   if (!seq_order) return KDA_ERR_NULL_ARG;
   return launch(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                 initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T,
-                H, D, stream, 0, 0, seq_order);
+                H, D, stream, 0, 0, seq_order, 0);
+}
+
+int kda_fwd_transposed_state(const void* q, const void* k, const void* v, const void* g,
+                             const void* beta, float scale, void* out, const float* A_log,
+                             const float* dt_bias, float lower_bound, const void* initial_state,
+                             int initial_state_dtype, void* final_state, int final_state_dtype,
+                             const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T,
+                             int64_t H, int64_t D, void* stream) {
+  return launch(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T,
+                H, D, stream, 0, 0, nullptr, 1);
 }
 
 int kda_longest_first(const int64_t* cu_seqlens, int64_t num_seqs, int32_t* seq_order,

@@ -411,12 +411,24 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) S[kt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (p.s_in == nullptr) return;
+    // lane: value vbase + 16 nt + l16, four consecutive keys (one 8- or 16-byte
+    // access in the [V, K] layout; four element accesses, coalesced across the
+    // lanes' consecutive values, in the [K, V] layout)
 #pragma unroll
     for (int kt = 0; kt < F::KT; ++kt)
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) {
-        const int64_t off =
-            sbase + (int64_t)(vbase + 16 * nt + l16) * D + key_of_row(16 * kt + 4 * lg);
+        const int64_t vrow = vbase + 16 * nt + l16;
+        const int64_t key0 = key_of_row(16 * kt + 4 * lg);
+        if (p.s_kv) {
+          const int64_t off = sbase + key0 * D + vrow;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            S[kt][nt][i] = p.s_in_fp32 ? static_cast<const float*>(p.s_in)[off + i * D]
+                                       : bf2f(static_cast<const u16*>(p.s_in)[off + i * D]);
+          continue;
+        }
+        const int64_t off = sbase + vrow * D + key0;
         if (p.s_in_fp32) {
           S[kt][nt] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.s_in) + off);
         } else {
@@ -432,9 +444,19 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     for (int kt = 0; kt < F::KT; ++kt)
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) {
-        const int64_t off =
-            sbase + (int64_t)(vbase + 16 * nt + l16) * D + key_of_row(16 * kt + 4 * lg);
+        const int64_t vrow = vbase + 16 * nt + l16;
+        const int64_t key0 = key_of_row(16 * kt + 4 * lg);
         const f32x4_t sv = S[kt][nt];
+        if (p.s_kv) {
+          const int64_t off = sbase + key0 * D + vrow;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (p.s_out_fp32) static_cast<float*>(p.s_out)[off + i * D] = sv[i];
+            else static_cast<u16*>(p.s_out)[off + i * D] = to_bf16(sv[i]);
+          }
+          continue;
+        }
+        const int64_t off = sbase + vrow * D + key0;
         if (p.s_out_fp32) {
           *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.s_out) + off) = sv;
         } else {

@@ -26,6 +26,7 @@ struct KdaParams {
   int32_t H;                // heads
   int32_t s_in_fp32;        // 1: initial state is fp32
   int32_t s_out_fp32;       // 1: final state is fp32
+  int32_t s_kv;             // 1: states are [N, H, K, V] (key-major) instead of [N, H, V, K]
   int32_t n_vtiles;         // value tiles per (sequence, head)
   float scale;              // output scale
   float lb2;                // lower_bound * log2(e)

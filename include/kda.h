@@ -147,6 +147,21 @@ int kda_fwd_ordered(const void* q, const void* k, const void* v, const void* g,
                     int64_t D, void* stream, const int32_t* seq_order);
 
 /*
+ * kda_fwd_transposed_state -- kda_fwd with both states in the transposed,
+ * key-major layout [num_seqs, H, D(k), D(v)]: element (v, k) of a head's
+ * state sits at k * D + v (FlashKDA's alternative state layout, its
+ * transpose-state-layout option).  Everything else, including the exact
+ * in-place alias, is exactly as kda_fwd; the results equal those of kda_fwd on
+ * transposed states bitwise.
+ */
+int kda_fwd_transposed_state(const void* q, const void* k, const void* v, const void* g,
+                             const void* beta, float scale, void* out, const float* A_log,
+                             const float* dt_bias, float lower_bound, const void* initial_state,
+                             int initial_state_dtype, void* final_state, int final_state_dtype,
+                             const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T,
+                             int64_t H, int64_t D, void* stream);
+
+/*
  * kda_longest_first -- writes the longest-first order of a packed batch for
  * kda_fwd_ordered: seq_order[i] is the index of the sequence with the i-th
  * largest length cu_seqlens[n+1] - cu_seqlens[n] (equal lengths keep their

@@ -97,3 +97,33 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(got[0], inp["out"]), rep
         assert torch.equal(got[1], inp["final_state"]), rep
+
+
+@pytest.mark.parametrize("D,state_in,state_out", [(128, "fp32", "fp32"), (128, "bf16", "fp32"),
+                                                  (64, "bf16", "bf16"), (32, "fp32", "bf16")])
+def test_transposed_state_layout_matches(D, state_in, state_out):
+    """States in the key-major [N,H,K,V] layout give bitwise the results of the [N,H,V,K]
+    layout on transposed copies, for every state dtype mix and value-tile schedule."""
+    w = Workload("kv", B=1, T=0, H=5, D=D, seed=23, lengths=[97, 0, 160, 31],
+                 state_in=state_in, state_out=state_out)
+    inp = make_inputs(w, device=DEV)
+    _fwd(inp)
+    torch.cuda.synchronize()
+    ref_out, ref_fin = inp["out"].clone(), inp["final_state"].clone()
+    s_in_t = inp["initial_state"].transpose(-1, -2).contiguous()
+    fin_t = torch.full_like(inp["final_state"], float("nan"))
+    inp["out"].fill_(float("nan"))
+    kda.kda_fwd_transposed_state(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                 inp["scale"], inp["out"], inp["A_log"], inp["dt_bias"],
+                                 inp["lower_bound"], s_in_t, fin_t, inp["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert torch.equal(inp["out"], ref_out)
+    assert torch.equal(fin_t.transpose(-1, -2), ref_fin)
+    # exact in-place alias in the transposed layout
+    if state_in == state_out:
+        st = inp["initial_state"].transpose(-1, -2).contiguous()
+        kda.kda_fwd_transposed_state(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                     inp["scale"], inp["out"], inp["A_log"], inp["dt_bias"],
+                                     inp["lower_bound"], st, st, inp["cu_seqlens"])
+        torch.cuda.synchronize()
+        assert torch.equal(st.transpose(-1, -2), ref_fin)
