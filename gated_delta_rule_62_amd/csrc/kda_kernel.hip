@@ -159,8 +159,12 @@ struct Cfg {
   static constexpr int EPV = C * VT / (NJW * 64);  // value row layout (job waves): elements per thread
   static constexpr int TPRV = VT / EPV;          // threads per value row
   static constexpr int SCOLS = D / NGW;          // column layout (g; gate waves): key columns per wave
-  static constexpr int SPASS = SCOLS / 16;       // passes of 16 columns: 8 pairs x 8 row groups
-  static constexpr int RPG = C / 8;              // chunk rows per row group
+  // A gate pass covers CPG column pairs by RG row groups (CPG * RG = 64 lanes): 16 x 4
+  // when a wave has at least 32 columns, else 8 x 8.
+  static constexpr int RG = SCOLS >= 32 ? 4 : 8;
+  static constexpr int CPG = 64 / RG;
+  static constexpr int SPASS = SCOLS / (2 * CPG);
+  static constexpr int RPG = C / RG;             // chunk rows per row group
   static constexpr int LDQ = D + 8;            // bf16 row stride of [C][D] tiles
   static constexpr int LDG = D + 4;            // fp32 row stride of the prefix tile
   static constexpr int LDR = D + 16;           // bf16 row stride of the [C][D] Kr tile
@@ -173,7 +177,7 @@ struct Cfg {
   static_assert(EPT == 4 || EPT == 8 || EPT == 16, "row layout");
   static_assert(EPV == 4 || EPV == 8 || EPV == 16, "value row layout");
   static_assert(TPR >= 2 && TPR <= 32, "row reduction: DPP inside rows, one cross-row step");
-  static_assert(SPASS >= 1 && SPASS * 16 * NGW == D, "column layout");
+  static_assert(SPASS >= 1 && SPASS * 2 * CPG * NGW == D, "column layout");
   static_assert(D % 32 == 0, "head dim");
   static_assert(NJW == 2 || NJW == 4 || NJW == 8, "job assignment");
   static_assert(C <= NJW * 64, "one beta per job thread");
@@ -580,11 +584,11 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
 
   // ======================= preparation ======================================
   // Column layout (g, gate, prefix; gate waves): pass ps covers key columns
-  // g_col0 + 16 ps and g_col0 + 16 ps + 1 (lane bits 0-2 pick the pair) and chunk
-  // rows g_row0 .. g_row0 + RPG - 1 (lane bits 3-5 pick one of eight row groups).
+  // g_col0 + 2 CPG ps and g_col0 + 2 CPG ps + 1 (lane % CPG picks the pair) and
+  // chunk rows g_row0 .. g_row0 + RPG - 1 (lane / CPG picks one of RG row groups).
   const int gw = (F::SPLIT && !is_state) ? 0 : wave;  // index among the gate waves
-  const int g_col0 = gw * F::SCOLS + 2 * (lane & 7);
-  const int g_rg = lane >> 3;
+  const int g_col0 = gw * F::SCOLS + 2 * (lane % F::CPG);
+  const int g_rg = lane / F::CPG;
   const int g_row0 = g_rg * F::RPG;
   // Row layout (q, k, operands; operand waves): chunk row r_row, positions r_col ..
   // r_col + EPT - 1.
@@ -600,7 +604,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   for (int ps = 0; ps < F::SPASS; ++ps)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
-      gate_add[ps][c] = gate_mul * p.dt_bias[(int64_t)h * D + g_col0 + 16 * ps + c];
+      gate_add[ps][c] = gate_mul * p.dt_bias[(int64_t)h * D + g_col0 + 2 * F::CPG * ps + c];
 
   // Raw inputs of the chunk to prepare next, in registers.  Buffer loads through a
   // descriptor bounded to the chunk's valid rows: rows past the end of the
@@ -623,7 +627,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
 #pragma unroll
       for (int i = 0; i < F::RPG; ++i)
         raw_g[ps][i] = __builtin_amdgcn_raw_buffer_load_b32(
-            rg, off_g + (uint32_t)i * row_bytes + 32u * ps, 0, 0);
+            rg, off_g + (uint32_t)i * row_bytes + 4u * F::CPG * ps, 0, 0);
   };
   auto load_vb = [&](int c) {
     const int64_t cs = s0 + (int64_t)c * C;
@@ -641,14 +645,26 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     buf_load<F::EPT>(make_rsrc(p.q + tok_elem, nb), off_qk, raw_q);
     buf_load<F::EPT>(make_rsrc(p.k + tok_elem, nb), off_qk, raw_k);
   };
-  // Exclusive prefix over the eight row groups (lanes c, c+8, ..., c+56) of a
-  // per-lane total t.  Row groups 2r and 2r+1 share the 16-lane row r: a DPP
+  // Exclusive prefix over the row groups of a per-lane total t.  With four groups
+  // each is one 16-lane row and the two lane swaps below combine them.  With eight
+  // (lanes c, c+8, ..., c+56) row groups 2r and 2r+1 share the 16-lane row r: a DPP
   // shift by 8 inside the row gives the odd group its even neighbour, a rotate by 8
   // gives both the row total; the four row totals are then combined across rows
   // with the lane-swap instructions (the 16-row swap gives [r0, r0, r2, r2] and
   // [r1, r1, r3, r3]; their sum swapped across the 32-lane halves gives r0 + r1
   // to rows 2 and 3).
   auto rowgroup_excl = [&](float t) -> float {
+    if constexpr (F::RG == 4) {
+      // four row groups, one per 16-lane row: the lane swaps alone combine them
+      const unsigned ab = __builtin_bit_cast(unsigned, t);
+      const auto sw16 = __builtin_amdgcn_permlane16_swap(ab, ab, false, false);
+      const float below = __builtin_bit_cast(float, (unsigned)sw16[0]);  // row r-1 for odd r
+      const float pair = below + __builtin_bit_cast(float, (unsigned)sw16[1]);
+      const unsigned pb = __builtin_bit_cast(unsigned, pair);
+      const auto sw32 = __builtin_amdgcn_permlane32_swap(pb, pb, false, false);
+      const float lower = __builtin_bit_cast(float, (unsigned)sw32[0]);  // r0 + r1
+      return ((lg & 1) ? below : 0.f) + (lg >= 2 ? lower : 0.f);
+    }
     const float in_row = __builtin_bit_cast(
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t), 0x118, 0xf, 0xf, true));
     const float rt = t + dpp_f<0x128>(t);
@@ -665,7 +681,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   auto gate = [&](Slot<F>& nxt, int nxt_valid) {
 #pragma unroll
     for (int ps = 0; ps < F::SPASS; ++ps) {
-      const int col = g_col0 + 16 * ps;
+      const int col = g_col0 + 2 * F::CPG * ps;
       float run0[F::RPG], run1[F::RPG];
       float t0 = 0.f, t1 = 0.f;
 #pragma unroll
@@ -683,12 +699,12 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
 #pragma unroll
       for (int i = 0; i < F::RPG; ++i)
         *reinterpret_cast<f32x2_t*>(&sm.G[g_row0 + i][col]) = f32x2_t{run0[i] + off0, run1[i] + off1};
-      // G_T is the last row, held by row group 7; the other groups write the same
+      // G_T is the last row, held by the last row group; the other groups write the same
       // expressions into a discarded half of each array (no branch).  The decay
       // vector a goes to the state's row order (col is even, so the pair stays
       // adjacent), 2^(G_T - Ca) stays in key order.
       const float gt0 = t0 + off0, gt1 = t1 + off1;
-      const int discard = (g_rg == 7) ? 0 : F::D;
+      const int discard = (g_rg == F::RG - 1) ? 0 : F::D;
       *reinterpret_cast<f32x2_t*>(&nxt.a[discard + row_of_key(col)]) =
           f32x2_t{__builtin_amdgcn_exp2f(gt0), __builtin_amdgcn_exp2f(gt1)};
       *reinterpret_cast<f32x2_t*>(&sm.gtc[discard + col]) =
