@@ -150,11 +150,7 @@ struct Cfg {
   static constexpr int JOB_BASE = SPLIT ? NSW : 0;
   static constexpr int NJW = NW - JOB_BASE;      // job waves (they also stage v and beta)
   static constexpr int NGW = SPLIT ? NSW : NW;   // gate waves: the state waves in the split
-  // waves that prepare the exponent-scaled operands: every wave, or only the job
-  // waves when there are eight of them
-  static constexpr int NBW = (SPLIT && NJW >= 8) ? NJW : NW;
-  static constexpr int BBASE = NW - NBW;
-  static constexpr int EPT = C * D / (NBW * 64); // row layout (q, k): positions per thread
+  static constexpr int EPT = C * D / (NW * 64);  // row layout (q, k; every wave): positions per thread
   static constexpr int TPR = D / EPT;            // threads per chunk row
   static constexpr int EPV = C * VT / (NJW * 64);  // value row layout (job waves): elements per thread
   static constexpr int TPRV = VT / EPV;          // threads per value row
@@ -366,8 +362,6 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   const bool is_job = wave >= F::JOB_BASE;     // uniform per wave
   const int jw = is_job ? wave - F::JOB_BASE : 0;        // index among the job waves
   const int jtid = is_job ? tid - F::JOB_BASE * 64 : 0;  // thread index among them
-  const bool is_bwave = wave >= F::BBASE;                   // prepares operands
-  const int btid = is_bwave ? tid - F::BBASE * 64 : 0;
 
   // ---- work item ---------------------------------------------------------
   const int vt_idx = blockIdx.x % p.n_vtiles;
@@ -592,8 +586,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   const int g_row0 = g_rg * F::RPG;
   // Row layout (q, k, operands; operand waves): chunk row r_row, positions r_col ..
   // r_col + EPT - 1.
-  const int r_row = btid / F::TPR;
-  const int r_col = (btid % F::TPR) * F::EPT;
+  const int r_row = tid / F::TPR;
+  const int r_col = (tid % F::TPR) * F::EPT;
   // Value row layout (job waves).
   const int v_row = jtid / F::TPRV;
   const int v_col = (jtid % F::TPRV) * F::EPV;
@@ -853,18 +847,15 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   const int c1st = nchunks > 1 ? 1 : 0;
   if constexpr (F::SPLIT) {
     if (is_state) {
-      constexpr bool ops = F::BBASE == 0;         // the state waves share the operands
       state_in();
       if (nchunks > 0) {
         load_g(0);
-        if (ops) load_qk(0);
+        load_qk(0);
         gate(sm.slot[0], chunk_valid(0));
         load_g(c1st);
         lds_barrier();
-        if (ops) {
-          prep_B(sm.slot[0]);
-          load_qk(c1st);
-        }
+        prep_B(sm.slot[0]);
+        load_qk(c1st);
         lds_barrier();
         for (int s = 0; s < nchunks; ++s) {
           Slot<F>& cur = sm.slot[s & 1];
@@ -879,7 +870,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
           state_R(cur);
           lds_barrier();
           state_B(cur, s0 + (int64_t)s * C, chunk_valid(s));
-          if (ops && more) {
+          if (more) {
             prep_B(nxt);
             load_qk(nxt2);
           }
