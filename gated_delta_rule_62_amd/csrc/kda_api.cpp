@@ -222,8 +222,8 @@ int kda_fwd_transposed_state(const void* q, const void* k, const void* v, const 
 
 int kda_longest_first(const int64_t* cu_seqlens, int64_t num_seqs, int32_t* seq_order,
                       void* stream) {
-  if (!cu_seqlens || !seq_order) return KDA_ERR_NULL_ARG;
   if (num_seqs < 1 || num_seqs > kda::kMaxOrderSeqs) return KDA_ERR_BAD_VARLEN;
+  if (!cu_seqlens || !seq_order) return KDA_ERR_NULL_ARG;
   const Range rc = make_range(cu_seqlens, (num_seqs + 1) * 8);
   const Range ro = make_range(seq_order, num_seqs * 4);
   if (overlaps(rc, ro)) return KDA_ERR_BAD_ALIAS;

@@ -170,8 +170,8 @@ int kda_fwd_transposed_state(const void* q, const void* k, const void* v, const 
  *   num_seqs    1 .. 8192 (KDA_ERR_BAD_VARLEN otherwise).
  *   seq_order   int32 [num_seqs] device array, written; must not overlap
  *               cu_seqlens (KDA_ERR_BAD_ALIAS).
- * Returns KDA_OK, KDA_ERR_NULL_ARG, KDA_ERR_BAD_VARLEN, KDA_ERR_BAD_ALIAS or
- * KDA_ERR_HIP.  An order depends only on the lengths, so one computation can
+ * Returns KDA_OK, KDA_ERR_BAD_VARLEN (checked first), KDA_ERR_NULL_ARG,
+ * KDA_ERR_BAD_ALIAS or KDA_ERR_HIP.  An order depends only on the lengths, so one computation can
  * serve every layer of a model that shares the batch.
  */
 int kda_longest_first(const int64_t* cu_seqlens, int64_t num_seqs, int32_t* seq_order,
