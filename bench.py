@@ -114,6 +114,9 @@ def main():
     ap.add_argument("--workload", default="batched")
     ap.add_argument("--chunk", type=int, default=None, help="force the chunk size")
     ap.add_argument("--v-tile", type=int, default=0, help="force the value tile")
+    ap.add_argument("--longest-first", action="store_true",
+                    help="packed workloads: dispatch sequences longest first (kda_fwd_ordered); "
+                         "the order is computed once, before the timed launches")
     ap.add_argument("--cpu-seconds", type=float, default=1.0,
                     help="minimum wall time of the CPU oracle baseline (whole-workload runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -139,7 +142,21 @@ def main():
     B, T, H, D = inp["q"].shape
     stream = torch.cuda.current_stream()
 
+    order = None
+    if args.longest_first:
+        if inp["cu_seqlens"] is None or chunk or args.v_tile:
+            print("--longest-first needs a packed workload and the automatic schedule",
+                  file=sys.stderr)
+            sys.exit(2)
+        order = kda.kda_longest_first(inp["cu_seqlens"], stream=stream)
+
     def step():
+        if order is not None:
+            kda.kda_fwd_ordered(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"],
+                                inp["out"], inp["A_log"], inp["dt_bias"], inp["lower_bound"],
+                                order, inp["initial_state"], inp["final_state"],
+                                inp["cu_seqlens"], stream=stream)
+            return
         kda.kda_fwd_sched(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"],
                           inp["out"], inp["A_log"], inp["dt_bias"], inp["lower_bound"],
                           inp["initial_state"], inp["final_state"], inp["cu_seqlens"],
@@ -182,7 +199,8 @@ def main():
                                "lower_bound=%g, state %s->%s" % (
                                    w.name, B, T, H, D, w.lower_bound, w.state_in, w.state_out),
                    "B": B, "T": T, "H": H, "D": D, "token_heads": token_heads(inp),
-                   "chunk": chunk or "auto", "v_tile": args.v_tile or "auto"},
+                   "chunk": chunk or "auto", "v_tile": args.v_tile or "auto",
+                   "sequence_order": "longest first" if order is not None else "index"},
         "mfma_pct_of_bf16_peak": 100.0 * tflops / MFMA_BF16_PEAK_TFLOPS,
         "kernel_ms": ms_per_launch,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
