@@ -120,6 +120,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=1.0,
                     help="minimum wall time of the CPU oracle baseline (whole-workload runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="after the timed launches, this many single launches each preceded by "
+                         "a 1 GiB fill that evicts the L2s and the Infinity Cache")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a known-size "
                          "kernel for scaling HBM byte counters)")
@@ -150,17 +153,21 @@ def main():
             sys.exit(2)
         order = kda.kda_longest_first(inp["cu_seqlens"], stream=stream)
 
-    def step():
-        if order is not None:
-            kda.kda_fwd_ordered(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"],
-                                inp["out"], inp["A_log"], inp["dt_bias"], inp["lower_bound"],
-                                order, inp["initial_state"], inp["final_state"],
-                                inp["cu_seqlens"], stream=stream)
-            return
-        kda.kda_fwd_sched(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"],
+    # The binding checks and marshals the arguments once; the timed loop then calls
+    # the C ABI directly, so host-side Python work never gaps the launches.
+    lib = kda.load_library()
+    args_c = kda._marshal(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"],
                           inp["out"], inp["A_log"], inp["dt_bias"], inp["lower_bound"],
-                          inp["initial_state"], inp["final_state"], inp["cu_seqlens"],
-                          chunk_size=chunk, v_tile=args.v_tile, stream=stream)
+                          inp["initial_state"], inp["final_state"], inp["cu_seqlens"], stream)
+    if order is not None:
+        call = lambda: lib.kda_fwd_ordered(*args_c, order.data_ptr())
+    else:
+        call = lambda: lib.kda_fwd_sched(*args_c, int(chunk), int(args.v_tile))
+
+    def step():
+        st = call()
+        if st != kda.KDA_OK:
+            raise kda.KdaError(st)
 
     for _ in range(args.warmup):
         step()
@@ -175,6 +182,33 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_launch = ev0.elapsed_time(ev1) / args.steps
+    # a second pass with an event between consecutive launches gives the median and
+    # minimum single launch (the event packets add a little time between launches,
+    # so the mean above is taken without them)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    singles = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+
+    cold = None
+    if args.cold_reps > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        cold_ms = []
+        for _ in range(args.cold_reps):
+            flush.fill_(1)
+            c0.record(stream)
+            step()
+            c1.record(stream)
+            torch.cuda.synchronize()
+            cold_ms.append(c0.elapsed_time(c1))
+        cold_ms.sort()
+        del flush
+        cold = cold_ms
     tokens = B * T
     value = tokens * args.steps / wall
 
@@ -203,11 +237,19 @@ def main():
                    "sequence_order": "longest first" if order is not None else "index"},
         "mfma_pct_of_bf16_peak": 100.0 * tflops / MFMA_BF16_PEAK_TFLOPS,
         "kernel_ms": ms_per_launch,
+        "kernel_ms_median": singles[len(singles) // 2],
+        "kernel_ms_min": singles[0],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
                      "algorithmic_bytes": nbytes, "counted_tflops": tflops},
         "kernel_source_hash": kernel_source_hash(),
     }
+    if cold is not None:
+        med = cold[len(cold) // 2]
+        result["cold_cache"] = {
+            "reps": len(cold), "kernel_ms_median": med, "kernel_ms_min": cold[0],
+            "hbm_frac_median": nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "note": "each launch after a 1 GiB fill that evicts the L2s and the Infinity Cache"}
     if args.calib_copy_mb:
         # One elementwise kernel of known traffic (torch.neg: reads and writes every
         # byte once) over a source evicted from the caches by a 1 GiB fill first.
