@@ -129,9 +129,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the KDA prefill kernel runs on a single "
-              "MI355X here and this build has no multi-GPU path (heads or sequences would be "
-              "sharded across GPUs with no exchange). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library runs one GPU's share of the work and "
+              "has no multi-GPU path (heads or sequences would be sharded across GPUs with no "
+              "exchange). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
