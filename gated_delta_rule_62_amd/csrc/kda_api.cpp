@@ -154,6 +154,16 @@ int launch(const void* q, const void* k, const void* v, const void* g, const voi
   p.s_out = final_state;
   p.cu = cu_seqlens;
   p.order = seq_order;
+  // Without a caller order, a packed batch whose workgroups outnumber the CUs by up
+  // to four times (so a few start only when others finish, and a long one starting
+  // last would set the time) is dispatched longest first by the kernel.  With more
+  // workgroups the dispatch already balances itself and the ranking would only cost.
+  const int64_t grid = num_seqs * H * (D / vt);
+  const int64_t cus = device_cus();
+  p.auto_order = (cu_seqlens != nullptr && seq_order == nullptr &&
+                  num_seqs <= kda::kMaxAutoOrderSeqs && grid > cus && grid <= 4 * cus)
+                     ? 1
+                     : 0;
   p.T = T;
   p.T_total = B * T;
   p.N = static_cast<int32_t>(num_seqs);

@@ -211,6 +211,7 @@ struct alignas(16) Smem {
   float G[F::C][F::LDG];     // inclusive base-2 decay prefix of the chunk being prepared
   float L[F::C][F::LDL];     // diagonal tiles of strictLower(diag(beta) Kc Ki^T)
   float gtc[2 * F::D];       // 2^(G_T - Ca) (second half: discarded writes)
+  int pick;                  // the sequence this workgroup takes (automatic order)
 };
 
 // Stores N consecutive bf16 (N in {4, 8, 16}) from packed words.
@@ -374,6 +375,32 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   if (p.order != nullptr) {
     const int o = p.order[n];
     n = o < 0 ? 0 : (o >= p.N ? p.N - 1 : o);
+  } else if (p.auto_order) {  // uniform
+    // Longest first without a caller order (packed batches of at most
+    // kMaxAutoOrderSeqs sequences whose workgroups outnumber the CUs): every
+    // workgroup ranks the lengths, ties by index, and takes the sequence whose rank
+    // is its slot.  Eight lanes share a candidate and sum its rank over their
+    // share of the others; the prefix tile, not in use yet, holds the lengths.
+    int* lens = reinterpret_cast<int*>(&sm.G[0][0]);
+    for (int i = tid; i < p.N; i += F::NTHR) {
+      const int64_t l = p.cu[i + 1] - p.cu[i];
+      lens[i] = l < 0 ? 0 : (l > 0x7fffffff ? 0x7fffffff : (int)l);
+    }
+    lds_barrier();
+    const int sub = lane & 7;
+    for (int base = 0; base < p.N; base += F::NTHR / 8) {
+      const int i = base + (tid >> 3);
+      const int li = i < p.N ? lens[i] : 0;
+      int r = 0;
+      for (int j = sub; j < p.N; j += 8) {
+        const int lj = lens[j];
+        r += (lj > li || (lj == li && j < i)) ? 1 : 0;
+      }
+      const float rank = group_sum<8>((float)r);  // exact: at most kMaxAutoOrderSeqs
+      if (i < p.N && sub == 0 && (int)rank == n) sm.pick = i;
+    }
+    lds_barrier();
+    n = sm.pick;
   }
   int64_t s0, s1;
   if (p.cu != nullptr) {

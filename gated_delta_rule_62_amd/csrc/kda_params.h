@@ -20,6 +20,7 @@ struct KdaParams {
   void* s_out;              // [N, H, D, D] bf16/fp32 or nullptr
   const int64_t* cu;        // [N+1] or nullptr (batched)
   const int32_t* order;     // [N] sequence order of the workgroups, or nullptr (identity)
+  int32_t auto_order;       // 1: no order given; the kernel dispatches longest first itself
   int64_t T;                // tokens per batch row (batched mode)
   int64_t T_total;          // B*T
   int32_t N;                // sequences
@@ -42,6 +43,9 @@ bool kda_schedule_supported(int D, int chunk, int v_tile);
 // Largest num_seqs the on-device longest-first ordering handles (one workgroup
 // sorts all lengths in LDS).
 constexpr int kMaxOrderSeqs = 8192;
+
+// Largest num_seqs for which the forward kernel ranks the lengths itself.
+constexpr int kMaxAutoOrderSeqs = 256;
 
 // Launches the longest-first ordering of num_seqs (<= kMaxOrderSeqs) sequences.
 hipError_t launch_longest_first(const int64_t* cu, int num_seqs, int32_t* order,

@@ -94,6 +94,12 @@ extern "C" {
  *   B, T, H, D     sizes; D in {32, 64, 128}.
  *   stream         a hipStream_t (NULL: the null stream).
  *
+ * Scheduling: a packed batch of at most 256 sequences whose workgroups (num_seqs *
+ * H * D / value tile) number between one and four times the device's compute
+ * units is dispatched longest first: the kernel ranks the lengths itself, so the
+ * host still reads nothing.  The order never changes the results (see
+ * kda_fwd_ordered for a caller-chosen order).
+ *
  * Returns KDA_OK or a negative status.  The decay span of a chunk is
  * chunk * |lower_bound| * log2(e); it must not exceed 236 (|lb| <= 10.22 with
  * 16-token chunks).  The library uses 32-token chunks when their span allows it

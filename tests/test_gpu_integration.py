@@ -63,6 +63,25 @@ def test_sequence_order_is_bitwise_neutral():
         assert torch.equal(inp["final_state"], ref[1]), order.tolist()
 
 
+def test_automatic_longest_first_is_bitwise_neutral():
+    """A packed batch whose workgroups outnumber the CUs makes kda_fwd rank the lengths
+    in the kernel and dispatch longest first; the results equal those of the identity
+    order bitwise (ties in length included)."""
+    lengths = [300, 700, 1024, 33, 0, 512, 33, 700]
+    w = Workload("auto_order", B=1, T=0, H=48, D=128, seed=27, lengths=lengths,
+                 state_in="bf16")
+    inp = make_inputs(w, device=DEV)
+    assert len(lengths) * 48 > 256  # more workgroups than compute units
+    _fwd(inp)
+    torch.cuda.synchronize()
+    ref = (inp["out"].clone(), inp["final_state"].clone())
+    inp["out"].fill_(float("nan"))
+    inp["final_state"].fill_(float("nan"))
+    _fwd(inp, torch.arange(len(lengths), dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(inp["out"], ref[0]) and torch.equal(inp["final_state"], ref[1])
+
+
 def test_graph_capture_replays_match_eager():
     """The forward records into a HIP graph (no host sync, no allocation, no memset in
     the call); each replay, with eager work and new input values in between, matches an
