@@ -156,9 +156,9 @@ def main():
     # The binding checks and marshals the arguments once; the timed loop then calls
     # the C ABI directly, so host-side Python work never gaps the launches.
     lib = kda.load_library()
-    args_c = kda._marshal(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"],
-                          inp["out"], inp["A_log"], inp["dt_bias"], inp["lower_bound"],
-                          inp["initial_state"], inp["final_state"], inp["cu_seqlens"], stream)
+    args_c = kda.c_args(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"],
+                        inp["out"], inp["A_log"], inp["dt_bias"], inp["lower_bound"],
+                        inp["initial_state"], inp["final_state"], inp["cu_seqlens"], stream)
     if order is not None:
         call = lambda: lib.kda_fwd_ordered(*args_c, order.data_ptr())
     else:

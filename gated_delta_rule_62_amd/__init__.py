@@ -14,7 +14,7 @@ import os
 from ._build import LIB_PATH, build  # noqa: F401  (build() is the in-tree compile step)
 
 __all__ = ["kda_fwd", "kda_fwd_sched", "kda_fwd_ordered", "kda_fwd_transposed_state",
-           "kda_longest_first", "kda_fwd_check",
+           "kda_longest_first", "kda_fwd_check", "c_args",
            "kda_chunk_anchor", "kda_status_string", "KdaError", "library_path", "load_library"]
 
 KDA_OK = 0
@@ -99,9 +99,11 @@ def _state_dtype_code(t):
     raise TypeError("state tensors must be bfloat16 or float32, got %s" % t.dtype)
 
 
-def _marshal(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
-             final_state, cu_seqlens, stream, extra=()):
-    """Checks the tensors and returns the C arguments shared by every forward entry point."""
+def c_args(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+           final_state, cu_seqlens, stream=None, extra=()):
+    """Checks the tensors and returns the C arguments shared by every forward entry point
+    (everything up to and including the stream), for callers that launch the C functions
+    of ``load_library()`` directly in a tight loop."""
     import torch
     acts = {"q": q, "k": k, "v": v, "g": g, "out": out}
     for name, t in acts.items():
@@ -157,8 +159,8 @@ def kda_fwd_sched(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
     cu_seqlens int64 ``[N+1]`` on the device (varlen, B == 1) or None (batched).
     ``stream`` defaults to torch's current stream on q's device.
     """
-    args = _marshal(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
-                    final_state, cu_seqlens, stream)
+    args = c_args(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                  final_state, cu_seqlens, stream)
     st = load_library().kda_fwd_sched(*args, int(chunk_size), int(v_tile))
     if st != KDA_OK:
         raise KdaError(st)
@@ -172,8 +174,8 @@ def kda_fwd_ordered(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, s
     import torch
     if seq_order.dtype != torch.int32 or seq_order.dim() != 1:
         raise ValueError("seq_order must be a 1-d int32 tensor")
-    args = _marshal(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
-                    final_state, cu_seqlens, stream, extra=(seq_order,))
+    args = c_args(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                  final_state, cu_seqlens, stream, extra=(seq_order,))
     if seq_order.numel() != args[15]:
         raise ValueError("seq_order must have one entry per sequence")
     st = load_library().kda_fwd_ordered(*args, seq_order.data_ptr())
@@ -185,8 +187,8 @@ def kda_fwd_transposed_state(q, k, v, g, beta, scale, out, A_log, dt_bias, lower
                              initial_state=None, final_state=None, cu_seqlens=None,
                              stream=None) -> None:
     """``kda_fwd`` with both states in the key-major layout ``[N,H,D(k),D(v)]``."""
-    args = _marshal(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
-                    final_state, cu_seqlens, stream)
+    args = c_args(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                  final_state, cu_seqlens, stream)
     st = load_library().kda_fwd_transposed_state(*args)
     if st != KDA_OK:
         raise KdaError(st)
