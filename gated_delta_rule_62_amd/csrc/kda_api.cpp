@@ -11,13 +11,11 @@
 namespace {
 
 constexpr double kLog2e = 1.4426950408889634;
-// Largest base-2 exponent a centred bf16 operand may reach: 2^126 keeps every
-// scaled operand (|kh| <= 1, scale included) below the bf16 maximum.
-constexpr double kMaxExp = 126.0;
-// Largest anchor magnitude: the kernel's unscaled products Kc S^T and S Qc^T
-// reach 2^-Ca times a state row's 1-norm, and 2^110 leaves fp32 room for rows up
-// to 2^18.
-constexpr double kMaxAnchor = 110.0;
+// Largest decay span (base 2) of a chunk.  The operands are centred on the middle
+// of the span, so they reach at most 2^(span/2) = 2^118 (|qh|, |kh| <= 1): 2^9
+// below the bf16 maximum, and the smallest of them, 2^-118 times a component,
+// keeps 8 binades above the bf16 normal minimum for the components' own range.
+constexpr double kMaxSpan = 236.0;
 
 struct Range {
   uintptr_t lo;
@@ -39,11 +37,7 @@ bool overlaps(Range a, Range b) {
 // Decay span (base 2) of a chunk: the largest magnitude of its prefix, chunk |lb| log2(e).
 double chunk_span(double lb, int chunk) { return chunk * std::fabs(lb) * kLog2e; }
 
-// The anchor Ca = min(0, 126 - span) lies in the bf16-safe window [-126, 126 - span];
-// it is admissible when -Ca <= 110, i.e. span <= 236.
-bool chunk_admissible(double lb, int chunk) {
-  return chunk_span(lb, chunk) <= kMaxExp + kMaxAnchor;
-}
+bool chunk_admissible(double lb, int chunk) { return chunk_span(lb, chunk) <= kMaxSpan; }
 
 int auto_chunk(double lb) { return chunk_admissible(lb, 32) ? 32 : 16; }
 
@@ -253,8 +247,7 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
 }
 
 float kda_chunk_anchor(float lower_bound, int chunk_size) {
-  const double a = kMaxExp - chunk_span(lower_bound, chunk_size);
-  return static_cast<float>(a < 0.0 ? a : 0.0);
+  return static_cast<float>(-0.5 * chunk_span(lower_bound, chunk_size));
 }
 
 const char* kda_status_string(int status) {

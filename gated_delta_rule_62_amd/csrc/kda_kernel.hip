@@ -6,7 +6,7 @@
 // resident too, section 6, in tensor memory; here it is the accumulator file).
 //
 // Per chunk of C tokens (FlashInfer PR #4262 summary, sections 1-3):
-//   1. load q, k, g, v, beta; L2-normalise q and k (scale folded into q);
+//   1. load q, k, g, v, beta; L2-normalise q and k;
 //      gate lam2 = lb*log2(e)*sigmoid(exp(A_log)*(g + dt_bias)) (base 2)
 //   2. inclusive prefix G over the chunk per key column; a = 2^G_T
 //   3. operands (bf16, round to nearest even):
@@ -25,12 +25,16 @@
 //      never formed: P^T = 2^Ca (Kc S^T) and O = 2^Ca (S Qc^T + U (2^-Ca Mqk)^T),
 //      the power of two applied to the fp32 results.
 //
-// Anchor.  The centred operands stay inside the bf16 range when
-// -126 <= Ca <= 126 + C b (b = lb log2(e), so C b bounds the prefix of a chunk).
-// The library takes the top of that interval, Ca = min(0, 126 + C b): Ki then
-// reaches at most 2^126 and Kc, Qc at most 2^-Ca, which keeps the unscaled
-// products Kc S^T and S Qc^T far from the fp32 range (the host limits -Ca to
-// 110, so state rows up to 2^18 in 1-norm are safe).
+// Anchor.  The prefix of a chunk lies in [C b, 0] (b = lb log2(e)); the anchor is
+// its middle, Ca = C b / 2 (section 2's 16 b for 32-token chunks), so the centred
+// operands span 2^(Ca) .. 2^(-Ca) times a component of qh or kh, at most 2^118
+// for the spans the host admits, with as much room above the bf16 normal minimum
+// as below its maximum.  The state side runs 2^16 below scale: the accumulators
+// hold S 2^-16 and the solve yields U 2^-16 (power-of-two factors folded into
+// the solve operands, exact), so the unscaled products S Qc^T and S Kc^T stay
+// inside fp32 for state rows up to 2^25 in 1-norm; 2^(Ca + 16) restores P and
+// O, and the state is rescaled once on load and store.  The output scale is
+// applied with that factor rather than folded into qh.
 //
 // Schedule.  Steps 1-5 only touch chunk-local data, step 6 is the strictly
 // ordered recurrence (section 3's scheduling property).  Waves 0..NSW-1 hold the
@@ -85,6 +89,10 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 
 constexpr float kLog2e = 1.4426950408889634f;
+// The state side runs 2^-kStateExp below scale (see the header comment).
+constexpr float kStateExp = 16.0f;
+constexpr float kStateDown = 1.0f / 65536.0f;  // 2^-kStateExp
+constexpr float kStateUp = 65536.0f;           // 2^kStateExp
 constexpr float kNormEps = 1e-6f;
 
 __device__ __forceinline__ float bf2f(u16 x) { return __uint_as_float((unsigned)x << 16); }
@@ -194,7 +202,8 @@ __device__ constexpr int job_wave(int j) {
 template <class F>
 struct alignas(16) Slot {
   u16 Kr[F::C][F::LDR];      // columns in state-row order (read transposed)
-  u16 SOL[F::C][F::LDC];     // [[X11, 0], [-L21, X22]]: X = (I + L)^-1 diagonal blocks
+  u16 SOL[F::C][F::LDC];     // X11 2^-16, X22 2^-16 (X = (I + L)^-1 diagonal blocks) and
+                             // -L21 2^16: the solve then yields U 2^-16
   u16 Mqk[F::C][F::LDC];
   u16 V[F::C][F::LDV];
   float a[2 * F::D];         // 2^G_T in state-row order (second half: discarded writes)
@@ -416,8 +425,9 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   const int nchunks = (int)((s1 - s0 + C - 1) / C);
   const uint32_t row_bytes = (uint32_t)(H * D * 2);
   const float Ca = p.anchor;
-  const float c1 = __builtin_amdgcn_exp2f(Ca);    // 2^Ca
-  const float c1i = __builtin_amdgcn_exp2f(-Ca);  // 2^-Ca
+  const float c1 = __builtin_amdgcn_exp2f(Ca + kStateExp);  // 2^(Ca + 16): restores P
+  const float c1o = c1 * p.scale;                           // ... and O, with the scale
+  const float c1i = __builtin_amdgcn_exp2f(-Ca);            // 2^-Ca
   auto chunk_valid = [&](int c) -> int {
     const int64_t rem = s1 - (s0 + (int64_t)c * C);
     return rem < C ? (int)rem : C;
@@ -449,17 +459,19 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
           const int64_t off = sbase + key0 * D + vrow;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            S[kt][nt][i] = p.s_in_fp32 ? static_cast<const float*>(p.s_in)[off + i * D]
-                                       : bf2f(static_cast<const u16*>(p.s_in)[off + i * D]);
+            S[kt][nt][i] = kStateDown *
+                           (p.s_in_fp32 ? static_cast<const float*>(p.s_in)[off + i * D]
+                                        : bf2f(static_cast<const u16*>(p.s_in)[off + i * D]));
           continue;
         }
         const int64_t off = sbase + vrow * D + key0;
         if (p.s_in_fp32) {
-          S[kt][nt] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.s_in) + off);
+          S[kt][nt] = kStateDown *
+                      *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.s_in) + off);
         } else {
           const u32x2_t w =
               *reinterpret_cast<const u32x2_t*>(static_cast<const u16*>(p.s_in) + off);
-          S[kt][nt] = f32x4_t{bflo(w[0]), bfhi(w[0]), bflo(w[1]), bfhi(w[1])};
+          S[kt][nt] = kStateDown * f32x4_t{bflo(w[0]), bfhi(w[0]), bflo(w[1]), bfhi(w[1])};
         }
       }
   };
@@ -471,7 +483,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       for (int nt = 0; nt < F::NTW; ++nt) {
         const int64_t vrow = vbase + 16 * nt + l16;
         const int64_t key0 = key_of_row(16 * kt + 4 * lg);
-        const f32x4_t sv = S[kt][nt];
+        const f32x4_t sv = kStateUp * S[kt][nt];
         if (p.s_kv) {
           const int64_t off = sbase + key0 * D + vrow;
 #pragma unroll
@@ -551,8 +563,9 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   // B: the blocked solve for U, the state update and the output of the current
   // chunk.  With INV = (I + L)^-1 = [[X11, 0], [X21, X22]] the solve U^T = INV R^T
   // runs as U_top = X11 R_top, U_bot = X22 (R_bot - L21 U_top), so X21 is never
-  // formed.  The output leaves as bf16 straight from the accumulators, through a
-  // descriptor bounded to the chunk's valid rows.
+  // formed; with the solve operands' power-of-two factors both halves come out
+  // as U 2^-16, the state's own scale.  The output leaves as bf16 straight from
+  // the accumulators, through a descriptor bounded to the chunk's valid rows.
   auto state_B = [&](Slot<F>& cur, int64_t cur_start, int cur_valid) {
     u32x4_t bU[F::NTW];
     {
@@ -593,7 +606,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       else bM = lds_op_pad(&cur.Mqk[l16][0], lg);
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) {
-        const f32x4_t o = c1 * mfma_k32(bU[nt], bM, O[ct][nt]);
+        const f32x4_t o = c1o * mfma_k32(bU[nt], bM, O[ct][nt]);
         // lane: token 16 ct + l16, values wv0 + 16 nt + 4 lg .. +3
         const u32x2_t w = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
         __builtin_amdgcn_raw_buffer_store_b64(
@@ -751,7 +764,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     }
     sq = group_sum<F::TPR>(sq);
     sk = group_sum<F::TPR>(sk);
-    const float rq = p.scale * __builtin_amdgcn_rsqf(sq + kNormEps);
+    const float rq = __builtin_amdgcn_rsqf(sq + kNormEps);
     const float rk = __builtin_amdgcn_rsqf(sk + kNormEps);
     // eight positions (one 16-byte store per operand) at a time
     constexpr int RUN = F::EPT < 8 ? F::EPT : 8;
@@ -807,7 +820,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     if (ti != tj) {
       // lower-left block: every entry is below the diagonal
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) cur.SOL[16 + 4 * lg + ii][j] = to_bf16(-b4[ii] * acc[ii]);
+      for (int ii = 0; ii < 4; ++ii)
+        cur.SOL[16 + 4 * lg + ii][j] = to_bf16(-kStateUp * b4[ii] * acc[ii]);
       return;
     }
 #pragma unroll
@@ -844,7 +858,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       for (int t = 0; t < 4; ++t) x[t] = __builtin_fmaf(-Lr[t][jj], xj, x[t]);
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) cur.SOL[base + gq + 4 * t][base + m] = to_bf16(x[t]);
+    for (int t = 0; t < 4; ++t) cur.SOL[base + gq + 4 * t][base + m] = to_bf16(kStateDown * x[t]);
   };
   auto chunk_matrices = [&](Slot<F>& cur) {
     if constexpr (F::CT == 2) {

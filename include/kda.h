@@ -19,7 +19,8 @@
  * products and an fp32 state that stays on chip for the whole sequence.
  * Within a chunk the decayed operands are centred on a fixed exponent anchor
  * (section 2 of the PR #4262 summary); the state rows' 1-norms must stay below
- * 2^18 for the centred state products to stay inside fp32.
+ * 2^25 for the centred state products to stay inside fp32, and q and k rows
+ * below an L2 norm of 1.8e19 (their sums of squares are fp32).
  *
  * Conventions for every entry point:
  *   - Every pointer argument except `stream` is a caller-owned DEVICE pointer
@@ -198,14 +199,12 @@ int kda_fwd_check(const void* q, const void* k, const void* v, const void* g, co
 
 /*
  * kda_chunk_anchor -- the fixed exponent anchor Ca (base 2) the library centres a
- * chunk's operands on: min(0, 126 - chunk_size * |lower_bound| * log2(e)).
- * Section 2 of the PR #4262 summary centres on the middle of the window,
- * 16 * lower_bound * log2(e) for 32-token chunks (about -115.42 for
- * lower_bound = -5); every anchor in [-126, 126 - span] keeps the centred
- * operands inside the bf16 range and gives the same products, and the library
- * takes the top of that window (about -104.83 for lower_bound = -5), which keeps
- * the operands it also uses for the state products as small as possible.
- * Pure host function.
+ * chunk's operands on: the middle of the chunk's decay span,
+ * chunk_size * lower_bound * log2(e) / 2.  For 32-token chunks this is section 2
+ * of the PR #4262 summary's 16 * lower_bound * log2(e) (about -115.42 for
+ * lower_bound = -5).  The centred operands then reach 2^(-Ca) at most and keep
+ * as much room above the bf16 normal minimum as below its maximum, which the
+ * most strongly decayed rows of a chunk need.  Pure host function.
  */
 float kda_chunk_anchor(float lower_bound, int chunk_size);
 

@@ -47,19 +47,20 @@ def test_status_strings(lib):
 
 
 def test_anchor_window(lib):
-    """The library anchor sits at the top of the bf16-safe window [-126, 126 - span]
-    (span = chunk |lb| log2 e) and never needs more than 2^110 of headroom."""
+    """The library anchor is the middle of a chunk's decay span, chunk lb log2(e) / 2:
+    the pages' 16 lb log2(e) for 32-token chunks, so the centred operands reach at most
+    2^118 at the largest span the host admits (236)."""
     log2e = 1.4426950408889634
     for lb in (-0.01, -0.5, -1.0, -3.0, -5.0, -5.1):
         for chunk in (16, 32):
             span = chunk * abs(lb) * log2e
             a = kda.kda_chunk_anchor(lb, chunk)
-            assert abs(a - min(0.0, 126.0 - span)) < 1e-4, (lb, chunk, a)
-            assert -126.0 <= a <= 126.0 - span + 1e-4
-            assert -a <= 110.0 + 1e-4
-    # lb = -5, 32-token chunks: 126 - 32 * 5 * log2(e) = -104.83
-    assert abs(kda.kda_chunk_anchor(-5.0, 32) + 104.8312) < 1e-3
-    assert kda.kda_chunk_anchor(-5.0, 16) == 0.0
+            assert abs(a + span / 2) < 1e-4, (lb, chunk, a)
+            assert -a <= 118.0 + 1e-4
+    # lb = -5, 32-token chunks: 16 * -5 * log2(e) = -115.42 (the pages' constant)
+    assert abs(kda.kda_chunk_anchor(-5.0, 32) - 16 * -5.0 * log2e) < 1e-4
+    assert abs(kda.kda_chunk_anchor(-5.0, 32) + 115.4156) < 1e-3
+    assert abs(kda.kda_chunk_anchor(-10.22, 16) + 117.96) < 1e-2
 
 
 # fake device addresses, far apart so that only deliberate overlaps overlap

@@ -190,11 +190,41 @@ def test_weak_decay():
     _check_against_oracle(inp, tag="lb=-0.1")
 
 
+@pytest.mark.parametrize("lb", [-5.11, -10.22])
+def test_saturated_gate_at_the_chunk_limits(lb):
+    """Every gate saturated (g = +30: lambda = lb for every token and key) at the largest
+    |lb| each chunk size admits: the decay span of a chunk fills the whole bf16 window
+    (236 binades), so the centred operands reach both ends of it."""
+    w = Workload("satgate", B=1, T=100, H=2, D=128, seed=28, lower_bound=lb, state_in="fp32",
+                 state_out="fp32")
+    inp = make_inputs(w, device=DEV)
+    inp["g"].fill_(30.0)
+    _check_against_oracle(inp, tag="saturated gate lb=%g" % lb)
+    assert torch.isfinite(inp["out"].float()).all()
+
+
+def test_gate_and_beta_extremes_and_zero_or_huge_rows():
+    """Sharp and flat gates (A_log = 5 and -5), beta logits of +-20, q and k rows that
+    are exactly zero (their normalised rows are zero) or scaled by 1e15 (normalisation
+    removes the scale; the fp32 sums of squares stay finite below row norms of 1.8e19)."""
+    w = Workload("extremes", B=1, T=96, H=2, D=128, seed=29, state_in="bf16")
+    inp = make_inputs(w, device=DEV)
+    inp["A_log"][0] = 5.0
+    inp["A_log"][1] = -5.0
+    inp["beta"][0, 10:20] = 20.0
+    inp["beta"][0, 20:30] = -20.0
+    inp["q"][0, 40:44] = 0.0
+    inp["k"][0, 44:48] = 0.0
+    inp["q"][0, 50:60] *= 1e15
+    inp["k"][0, 60:70] *= 1e15
+    _check_against_oracle(inp, tag="extremes")
+
+
 def test_large_state_magnitude():
     # The kernel forms the state products from the centred operands and rescales the
     # fp32 results by a power of two; the unscaled products grow with the state's row
     # norms.  A fp32 state ~ N(0, 40^2) (row 1-norms near 4e3) and values scaled by
-    # 50 keep every row well inside the documented 2^18 bound.
+    # 50 keep every row well inside the documented 2^25 bound.
     # The absolute max-abs bound is scaled with the data (rel-L2 is scale-free).
     w = Workload("bigstate", B=1, T=200, H=2, D=128, seed=16, state_in="fp32", state_out="fp32")
     inp = make_inputs(w, device=DEV)
