@@ -226,14 +226,39 @@ def test_large_state_magnitude():
     # norms.  A fp32 state ~ N(0, 40^2) (row 1-norms near 4e3) and values scaled by
     # 50 keep every row well inside the documented 2^25 bound.
     # The absolute max-abs bound is scaled with the data (rel-L2 is scale-free).
-    w = Workload("bigstate", B=1, T=200, H=2, D=128, seed=16, state_in="fp32", state_out="fp32")
+    # A second case puts the rows near 2^23.7 in 1-norm (state ~ N(0, 2^17 * 0.1^2 ...)),
+    # under saturated gates at lb = -5, where the centred operands are largest.
+    for tag, s_mul, v_mul, g_fill in (("large state", 400.0, 50.0, None),
+                                      ("near-bound state", 2.0 ** 20, 2.0 ** 14, 30.0)):
+        w = Workload("bigstate", B=1, T=200, H=2, D=128, seed=16, state_in="fp32",
+                     state_out="fp32")
+        inp = make_inputs(w, device=DEV)
+        inp["initial_state"].mul_(s_mul)
+        inp["v"].mul_(v_mul)
+        if g_fill is not None:
+            inp["g"].fill_(g_fill)
+        _run(inp)
+        out_ref, fin_ref = _oracle(inp)
+        for what, x, ref in (("%s out" % tag, inp["out"], out_ref),
+                             ("%s final_state" % tag, inp["final_state"], fin_ref)):
+            mx, rel = _errors(x, ref)
+            peak = float(np.abs(ref).max())
+            print("%s: max-abs %.3e (peak %.3e) rel-L2 %.3e" % (what, mx, peak, rel), flush=True)
+            assert mx <= MAX_ABS * peak and rel <= REL_L2, what
+
+
+def test_large_scale_and_huge_rows():
+    """An output scale of 1e4 (applied with the final rescale, never folded into the
+    operands) and q/k rows scaled by 1e18 (sums of squares near 1.3e38, inside fp32)."""
+    w = Workload("scale", B=1, T=80, H=2, D=128, seed=30, state_in="bf16")
     inp = make_inputs(w, device=DEV)
-    inp["initial_state"].mul_(400.0)
-    inp["v"].mul_(50.0)
+    inp["scale"] = 1e4
+    inp["q"][0, 5:15] *= 1e18
+    inp["k"][0, 20:30] *= 1e18
     _run(inp)
     out_ref, fin_ref = _oracle(inp)
-    for what, x, ref in (("large state out", inp["out"], out_ref),
-                         ("large state final_state", inp["final_state"], fin_ref)):
+    for what, x, ref in (("scale 1e4 out", inp["out"], out_ref),
+                         ("scale 1e4 final_state", inp["final_state"], fin_ref)):
         mx, rel = _errors(x, ref)
         peak = float(np.abs(ref).max())
         print("%s: max-abs %.3e (peak %.3e) rel-L2 %.3e" % (what, mx, peak, rel), flush=True)
