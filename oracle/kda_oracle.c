@@ -13,7 +13,9 @@
  *             lower_bound and the per-token range [lb, 0] -- FlashInfer PR #4262
  *             summary, section 2 "Chunk-32 Through Fixed-Anchor Exponent
  *             Centering" and section 12 "Strict Dispatch and Safe Fallback";
- *             the formula itself is a reading, see the test suite's gate pins)
+ *             the formula itself is a reading: parity unpinned against any
+ *             printed gate values, since no page prints one; its closed-form
+ *             values, limits and range are pinned by the test suite)
  *   norms     qh_t = q_t / sqrt(|q_t|^2 + eps),  kh_t = k_t / sqrt(|k_t|^2 + eps)
  *             (in-kernel Q/K L2 normalisation, section 12 of the same page)
  *   beta      b_t = sigmoid(beta_t)   (the beta input is a logit, section 12)
