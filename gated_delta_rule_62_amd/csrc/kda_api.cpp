@@ -70,8 +70,12 @@ int resolve(const void* q, const void* k, const void* v, const void* g, const vo
   if (B < 1 || H < 1 || T < 0) return KDA_ERR_BAD_SHAPE;
   if (T == 0 && cu_seqlens == nullptr) return KDA_ERR_BAD_SHAPE;
   if (D != 32 && D != 64 && D != 128) return KDA_ERR_BAD_SHAPE;
-  // the kernels address one chunk (up to 32 token rows) with 32-bit byte offsets
-  if (H * D * 2 * 32 >= ((int64_t)1 << 31) || B * T > ((int64_t)1 << 40)) return KDA_ERR_BAD_SHAPE;
+  // The kernels address one chunk (up to 32 token rows) with 32-bit byte offsets:
+  // H * D * 64 < 2^31.  Every size test is a division, so no product of caller
+  // sizes is formed before it is known to fit (64 D divides 2^31 exactly).
+  if (H >= ((int64_t)1 << 31) / (64 * D) || T > ((int64_t)1 << 40) / B) return KDA_ERR_BAD_SHAPE;
+  // activation extents below 2^62 bytes, so the range arithmetic cannot wrap
+  if (B * T > ((int64_t)1 << 62) / (H * D * 2)) return KDA_ERR_BAD_SHAPE;
   if (initial_state && initial_state_dtype != KDA_DTYPE_BF16 &&
       initial_state_dtype != KDA_DTYPE_FP32)
     return KDA_ERR_BAD_DTYPE;
@@ -82,7 +86,7 @@ int resolve(const void* q, const void* k, const void* v, const void* g, const vo
   } else {
     if (num_seqs != B) return KDA_ERR_BAD_VARLEN;
   }
-  if (num_seqs * H > ((int64_t)1 << 31) / 4) return KDA_ERR_BAD_SHAPE;
+  if (num_seqs > (((int64_t)1 << 31) / 4) / H) return KDA_ERR_BAD_SHAPE;  // num_seqs H <= 2^29
   if (!std::isfinite(scale)) return KDA_ERR_BAD_SCALE;
   if (!std::isfinite(lower_bound) || !(lower_bound < 0.f)) return KDA_ERR_BAD_LOWER_BOUND;
 

@@ -46,7 +46,9 @@ extern "C" {
 #define KDA_OK 0
 #define KDA_ERR_NULL_ARG (-1)        /* a required pointer is NULL                      */
 #define KDA_ERR_BAD_SHAPE (-2)       /* B,T,H < 1 (T may be 0 only with cu_seqlens),     */
-                                     /* D not in {32, 64, 128}, or H * D >= 2^25          */
+                                     /* D not in {32, 64, 128}, H * D >= 2^25,            */
+                                     /* B * T > 2^40, num_seqs * H > 2^29, or an          */
+                                     /* activation tensor of more than 2^62 bytes         */
 #define KDA_ERR_BAD_DTYPE (-3)       /* unknown state dtype code                         */
 #define KDA_ERR_BAD_VARLEN (-4)      /* cu_seqlens with B != 1, num_seqs < 1, or         */
                                      /* num_seqs != B without cu_seqlens                 */

@@ -106,6 +106,26 @@ def test_null_and_shape_errors(lib):
         assert _check(D=D) == kda.KDA_ERR_BAD_SHAPE
 
 
+def test_size_limits_reject_without_overflow(lib):
+    """Sizes whose products would overflow 64 bits are rejected as shapes, never wrapped;
+    sizes just inside each limit pass the shape checks."""
+    bad = kda.KDA_ERR_BAD_SHAPE
+    assert _check(B=1 << 40, T=1 << 40) == bad                  # B T = 2^80
+    assert _check(B=1, T=(1 << 40) + 1) == bad
+    assert _check(B=1, T=1 << 40) != bad
+    assert _check(H=1 << 62) == bad
+    assert _check(H=1 << 18, D=128) == bad                      # H D = 2^25
+    assert _check(H=(1 << 18) - 1, D=128) != bad
+    assert _check(H=1 << 20, D=32) == bad
+    assert _check(B=1, T=1 << 40, H=(1 << 20) - 1, D=32) == bad  # ~2^65 activation bytes
+    assert _check(B=1, T=(1 << 37) + 1, H=1 << 19, D=32) == bad  # just over 2^62 bytes
+    assert _check(B=1, T=1 << 37, H=1 << 19, D=32) != bad        # exactly 2^62 bytes
+    assert _check(B=1, T=100, N=1 << 62, has_cu=True) == bad     # num_seqs H overflows
+    assert _check(B=1, T=100, N=(1 << 27) + 1, H=4, has_cu=True) == bad
+    assert _check(B=1, T=100, N=1 << 27, H=4, has_cu=True, has_s_in=False,
+                  has_s_out=False) == kda.KDA_OK                 # num_seqs H = 2^29
+
+
 def test_dtype_and_varlen_errors(lib):
     assert _check(in_dt=2) == kda.KDA_ERR_BAD_DTYPE
     assert _check(out_dt=-1) == kda.KDA_ERR_BAD_DTYPE
