@@ -99,11 +99,18 @@ def _state_dtype_code(t):
     raise TypeError("state tensors must be bfloat16 or float32, got %s" % t.dtype)
 
 
+def _on_device(t):
+    """The library launches on the current HIP device: make t's device current."""
+    import torch
+    return torch.cuda.device(t.device)
+
+
 def c_args(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
            final_state, cu_seqlens, stream=None, extra=()):
     """Checks the tensors and returns the C arguments shared by every forward entry point
     (everything up to and including the stream), for callers that launch the C functions
-    of ``load_library()`` directly in a tight loop."""
+    of ``load_library()`` directly in a tight loop.  Such callers make the tensors' device
+    current themselves (``torch.cuda.device``): the library launches on the current one."""
     import torch
     acts = {"q": q, "k": k, "v": v, "g": g, "out": out}
     for name, t in acts.items():
@@ -161,7 +168,8 @@ def kda_fwd_sched(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
     """
     args = c_args(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                   final_state, cu_seqlens, stream)
-    st = load_library().kda_fwd_sched(*args, int(chunk_size), int(v_tile))
+    with _on_device(q):
+        st = load_library().kda_fwd_sched(*args, int(chunk_size), int(v_tile))
     if st != KDA_OK:
         raise KdaError(st)
 
@@ -178,7 +186,8 @@ def kda_fwd_ordered(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, s
                   final_state, cu_seqlens, stream, extra=(seq_order,))
     if seq_order.numel() != args[15]:
         raise ValueError("seq_order must have one entry per sequence")
-    st = load_library().kda_fwd_ordered(*args, seq_order.data_ptr())
+    with _on_device(q):
+        st = load_library().kda_fwd_ordered(*args, seq_order.data_ptr())
     if st != KDA_OK:
         raise KdaError(st)
 
@@ -189,7 +198,8 @@ def kda_fwd_transposed_state(q, k, v, g, beta, scale, out, A_log, dt_bias, lower
     """``kda_fwd`` with both states in the key-major layout ``[N,H,D(k),D(v)]``."""
     args = c_args(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                   final_state, cu_seqlens, stream)
-    st = load_library().kda_fwd_transposed_state(*args)
+    with _on_device(q):
+        st = load_library().kda_fwd_transposed_state(*args)
     if st != KDA_OK:
         raise KdaError(st)
 
@@ -211,8 +221,9 @@ def kda_longest_first(cu_seqlens, seq_order=None, stream=None):
     if stream is None:
         stream = torch.cuda.current_stream(cu_seqlens.device)
     s_ptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    st = load_library().kda_longest_first(cu_seqlens.data_ptr(), N, seq_order.data_ptr()
-                                          if N > 0 else None, s_ptr)
+    with _on_device(cu_seqlens):
+        st = load_library().kda_longest_first(cu_seqlens.data_ptr(), N, seq_order.data_ptr()
+                                              if N > 0 else None, s_ptr)
     if st != KDA_OK:
         raise KdaError(st)
     return seq_order

@@ -25,6 +25,8 @@
  * Conventions for every entry point:
  *   - Every pointer argument except `stream` is a caller-owned DEVICE pointer
  *     to contiguous memory; the library never frees or retains it.
+ *   - Kernels launch on the calling thread's current HIP device: the pointers
+ *     and `stream` must belong to it (hipSetDevice before the call).
  *   - The library allocates nothing and keeps no global state; calls on
  *     different streams may run concurrently.
  *   - kda_fwd is asynchronous: it validates on the host, enqueues one kernel on
