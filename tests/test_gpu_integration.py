@@ -82,23 +82,42 @@ def test_automatic_longest_first_is_bitwise_neutral():
     assert torch.equal(inp["out"], ref[0]) and torch.equal(inp["final_state"], ref[1])
 
 
-def test_graph_capture_replays_match_eager():
+@pytest.mark.parametrize("case", ["small_grid", "ranked_in_kernel", "ordered"])
+def test_graph_capture_replays_match_eager(case):
     """The forward records into a HIP graph (no host sync, no allocation, no memset in
     the call); each replay, with eager work and new input values in between, matches an
-    eager call on the same inputs bitwise."""
-    w = Workload("graph", B=1, T=0, H=4, D=128, seed=22, lengths=[200, 64, 333],
-                 state_in="bf16")
+    eager call on the same inputs bitwise.  Cases: a grid smaller than the GPU; a packed
+    batch of 5 sequences x 96 heads (480 workgroups), which the kernel dispatches longest
+    first by its own ranking; and the ordering kernel followed by the ordered forward,
+    both in the graph."""
+    if case == "small_grid":
+        w = Workload("graph", B=1, T=0, H=4, D=128, seed=22, lengths=[200, 64, 333],
+                     state_in="bf16")
+    else:
+        w = Workload("graph", B=1, T=0, H=96, D=128, seed=22, lengths=[200, 64, 333, 90, 17],
+                     state_in="bf16")
     inp = make_inputs(w, device=DEV)
+    order = torch.empty(len(w.lengths), dtype=torch.int32, device=DEV)
+
+    def call():
+        if case == "ordered":
+            kda.kda_longest_first(inp["cu_seqlens"], order)
+            _fwd(inp, order)
+        else:
+            _fwd(inp)
+
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        _fwd(inp)  # warm-up on the capture stream's side, as graph capture expects
+        call()  # warm-up on the capture stream's side, as graph capture expects
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        _fwd(inp)
+        call()
     torch.cuda.synchronize()
+    if case == "ordered":
+        assert order.cpu().tolist() == _expected_order(w.lengths)
     gen = torch.Generator(device=DEV).manual_seed(5)
     for rep in range(3):
         # new values in the captured input buffers (eager work between replays)
