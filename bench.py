@@ -122,7 +122,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="after the timed launches, this many single launches each preceded by "
-                         "a 1 GiB fill that evicts the L2s and the Infinity Cache")
+                         "a 1 GiB read sweep that evicts the L2s and the Infinity Cache (and as "
+                         "many after a 1 GiB fill)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a known-size "
                          "kernel for scaling HBM byte counters)")
@@ -193,22 +194,33 @@ def main():
     torch.cuda.synchronize()
     singles = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
 
-    cold = None
+    cold = cold_dirty = None
     if args.cold_reps > 0:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        # Cold caches, two ways.  Each timed launch follows a 1 GiB sweep that evicts
+        # the L2s and the 256 MB Infinity Cache.  A read sweep (a sum) leaves clean
+        # lines behind, so the launch pays only for its own misses.  A write sweep
+        # (a fill) leaves dirty lines, whose write-back the launch then also pays for.
+        flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
+        flush.fill_(1)
+        flush.sum()
+        torch.cuda.synchronize()
         c0 = torch.cuda.Event(enable_timing=True)
         c1 = torch.cuda.Event(enable_timing=True)
-        cold_ms = []
-        for _ in range(args.cold_reps):
-            flush.fill_(1)
-            c0.record(stream)
-            step()
-            c1.record(stream)
-            torch.cuda.synchronize()
-            cold_ms.append(c0.elapsed_time(c1))
-        cold_ms.sort()
+
+        def timed_after(sweep):
+            ms = []
+            for _ in range(args.cold_reps):
+                sweep()
+                c0.record(stream)
+                step()
+                c1.record(stream)
+                torch.cuda.synchronize()
+                ms.append(c0.elapsed_time(c1))
+            return sorted(ms)
+
+        cold = timed_after(lambda: flush.sum())
+        cold_dirty = timed_after(lambda: flush.fill_(1))
         del flush
-        cold = cold_ms
     tokens = B * T
     value = tokens * args.steps / wall
 
@@ -246,10 +258,16 @@ def main():
     }
     if cold is not None:
         med = cold[len(cold) // 2]
+        med_d = cold_dirty[len(cold_dirty) // 2]
         result["cold_cache"] = {
             "reps": len(cold), "kernel_ms_median": med, "kernel_ms_min": cold[0],
             "hbm_frac_median": nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "note": "each launch after a 1 GiB fill that evicts the L2s and the Infinity Cache"}
+            "note": "each launch after a 1 GiB read sweep that evicts the L2s and the "
+                    "Infinity Cache and leaves clean lines",
+            "after_write_sweep": {"kernel_ms_median": med_d, "kernel_ms_min": cold_dirty[0],
+                                  "hbm_frac_median": nbytes / (med_d * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                  "note": "each launch after a 1 GiB fill: the launch also "
+                                          "writes back the fill's dirty lines"}}
     if args.calib_copy_mb:
         # One elementwise kernel of known traffic (torch.neg: reads and writes every
         # byte once) over a source evicted from the caches by a 1 GiB fill first.

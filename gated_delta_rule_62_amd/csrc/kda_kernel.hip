@@ -74,6 +74,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kda_params.h"
 
 namespace kda {
@@ -217,7 +219,10 @@ struct alignas(16) Smem {
                              // matrices and preparation alternate in them
   u16 Kc[F::C][F::LDQ];
   u16 Ki[F::C][F::LDQ];
-  float G[F::C][F::LDG];     // inclusive base-2 decay prefix of the chunk being prepared
+  float G[F::C][F::LDG];     // inclusive base-2 decay prefix of the chunk being prepared,
+                             // inside its row group of the gate layout
+  float Goff[F::RG][F::D];   // ... plus this per row group and key: the prefix of the
+                             // earlier row groups, minus the anchor
   float L[F::C][F::LDL];     // diagonal tiles of strictLower(diag(beta) Kc Ki^T)
   float gtc[2 * F::D];       // 2^(G_T - Ca) (second half: discarded writes)
   int pick;                  // the sequence this workgroup takes (automatic order)
@@ -712,7 +717,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     return in_row + ((lg & 1) ? below : 0.f) + (lg >= 2 ? lower : 0.f);
   };
   // A (gate waves): gate and inclusive prefix of the next chunk (column layout).
-  auto gate = [&](Slot<F>& nxt, int nxt_valid) {
+  auto gate_rows = [&](Slot<F>& nxt, int nxt_valid, auto full) {
 #pragma unroll
     for (int ps = 0; ps < F::SPASS; ++ps) {
       const int col = g_col0 + 2 * F::CPG * ps;
@@ -720,7 +725,9 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       float t0 = 0.f, t1 = 0.f;
 #pragma unroll
       for (int i = 0; i < F::RPG; ++i) {
-        const float lbv = g_row0 + i < nxt_valid ? p.lb2 : 0.f;  // no decay past the sequence
+        float lbv = p.lb2;
+        if constexpr (!decltype(full)::value)
+          lbv = g_row0 + i < nxt_valid ? p.lb2 : 0.f;  // no decay past the sequence
         const float z0 = __builtin_fmaf(bflo(raw_g[ps][i]), gate_mul, gate_add[ps][0]);
         const float z1 = __builtin_fmaf(bfhi(raw_g[ps][i]), gate_mul, gate_add[ps][1]);
         t0 = __builtin_fmaf(lbv, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z0)), t0);
@@ -730,9 +737,12 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       }
       const float off0 = rowgroup_excl(t0);
       const float off1 = rowgroup_excl(t1);
+      // the prefix inside the row group, and the row group's offset (minus the
+      // anchor) once per key: the operand preparation adds the two
 #pragma unroll
       for (int i = 0; i < F::RPG; ++i)
-        *reinterpret_cast<f32x2_t*>(&sm.G[g_row0 + i][col]) = f32x2_t{run0[i] + off0, run1[i] + off1};
+        *reinterpret_cast<f32x2_t*>(&sm.G[g_row0 + i][col]) = f32x2_t{run0[i], run1[i]};
+      *reinterpret_cast<f32x2_t*>(&sm.Goff[g_rg][col]) = f32x2_t{off0 - Ca, off1 - Ca};
       // G_T is the last row, held by the last row group; the other groups write the same
       // expressions into a discarded half of each array (no branch).  The decay
       // vector a goes to the state's row order (col is even, so the pair stays
@@ -744,6 +754,12 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       *reinterpret_cast<f32x2_t*>(&sm.gtc[discard + col]) =
           f32x2_t{__builtin_amdgcn_exp2f(gt0 - Ca), __builtin_amdgcn_exp2f(gt1 - Ca)};
     }
+  };
+  // A (gate waves): gate and inclusive prefix of the next chunk (column layout);
+  // a full chunk (the common case) skips the per-row end-of-sequence mask.
+  auto gate = [&](Slot<F>& nxt, int nxt_valid) {
+    if (nxt_valid == C) gate_rows(nxt, nxt_valid, std::true_type{});
+    else gate_rows(nxt, nxt_valid, std::false_type{});
   };
   // A (job waves): value tile and beta of the next chunk.
   auto stage_vb = [&](Slot<F>& nxt, int nxt_valid) {
@@ -775,12 +791,13 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       for (int j = 0; j < RUN / 4; ++j) {
         const int key = r_col + r0 + 4 * j;
         const f32x4_t gg = *reinterpret_cast<const f32x4_t*>(&sm.G[r_row][key]);
+        const f32x4_t go = *reinterpret_cast<const f32x4_t*>(&sm.Goff[r_row / F::RPG][key]);
         const f32x4_t tt = *reinterpret_cast<const f32x4_t*>(&sm.gtc[key]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int x = 4 * j + e;
           const float qv = qn[r0 + x] * rq, kv = kn[r0 + x] * rk;
-          const float d = gg[e] - Ca;
+          const float d = gg[e] + go[e];                // G - Ca
           const float e1 = __builtin_amdgcn_exp2f(d);   // 2^(G - Ca)
           const float e2 = __builtin_amdgcn_exp2f(-d);  // 2^(Ca - G)
           oQc[x] = qv * e1;
