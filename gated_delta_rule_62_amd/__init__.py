@@ -164,6 +164,8 @@ def kda_fwd_sched(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
     q, k, v, g, out: bf16 ``[B,T,H,D]``; beta bf16 ``[B,T,H]``; A_log fp32 ``[H]``;
     dt_bias fp32 ``[H,D]``; states ``[N,H,D,D]`` bf16 or fp32 (or None);
     cu_seqlens int64 ``[N+1]`` on the device (varlen, B == 1) or None (batched).
+    ``chunk_size`` 0 (the longest admissible) or tokens per chunk (32, 16, 8, 4, 2, 1);
+    ``v_tile`` 0 (automatic) or the value rows per workgroup.
     ``stream`` defaults to torch's current stream on q's device.
     """
     args = c_args(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,

@@ -39,7 +39,21 @@ double chunk_span(double lb, int chunk) { return chunk * std::fabs(lb) * kLog2e;
 
 bool chunk_admissible(double lb, int chunk) { return chunk_span(lb, chunk) <= kMaxSpan; }
 
-int auto_chunk(double lb) { return chunk_admissible(lb, 32) ? 32 : 16; }
+// Tokens per chunk: 32 or 16 fill a 32- or 16-row tile; 8, 4, 2 and 1 run in a
+// 16-row tile whose last rows stay empty, which narrows the chunk's decay span for
+// strongly negative lower bounds.
+bool chunk_rows_valid(int rows) {
+  return rows == 32 || rows == 16 || rows == 8 || rows == 4 || rows == 2 || rows == 1;
+}
+int tile_rows(int rows) { return rows == 32 ? 32 : 16; }
+
+// The longest admissible chunk, or 0 when even one token's span is too wide
+// (|lb| above 236 / log2(e) = 163.6).
+int auto_chunk(double lb) {
+  for (int rows = 32; rows >= 1; rows /= 2)
+    if (chunk_admissible(lb, rows)) return rows;
+  return 0;
+}
 
 // Compute units of the current device (256 on MI355X when the query fails, e.g.
 // without a GPU).
@@ -91,11 +105,15 @@ int resolve(const void* q, const void* k, const void* v, const void* g, const vo
   if (!std::isfinite(lower_bound) || !(lower_bound < 0.f)) return KDA_ERR_BAD_LOWER_BOUND;
 
   int chunk = chunk_size;
-  if (chunk == 0) chunk = auto_chunk(lower_bound);
-  if (chunk != 16 && chunk != 32) return KDA_ERR_BAD_SCHEDULE;
+  if (chunk == 0) {
+    chunk = auto_chunk(lower_bound);
+    if (chunk == 0) return KDA_ERR_BAD_LOWER_BOUND;
+  }
+  if (!chunk_rows_valid(chunk)) return KDA_ERR_BAD_SCHEDULE;
   if (!chunk_admissible(lower_bound, chunk)) return KDA_ERR_BAD_LOWER_BOUND;
-  int vt = v_tile == 0 ? auto_v_tile(D, chunk, num_seqs * H) : v_tile;
-  if (!kda::kda_schedule_supported(static_cast<int>(D), chunk, vt)) return KDA_ERR_BAD_SCHEDULE;
+  const int tile = tile_rows(chunk);
+  int vt = v_tile == 0 ? auto_v_tile(D, tile, num_seqs * H) : v_tile;
+  if (!kda::kda_schedule_supported(static_cast<int>(D), tile, vt)) return KDA_ERR_BAD_SCHEDULE;
 
   // Buffer extents and the aliasing contract.
   const int64_t tok = B * T;
@@ -170,11 +188,12 @@ int launch(const void* q, const void* k, const void* v, const void* g, const voi
   p.s_out_fp32 = final_state_dtype == KDA_DTYPE_FP32 ? 1 : 0;
   p.s_kv = state_kv;
   p.n_vtiles = static_cast<int32_t>(D / vt);
+  p.chunk_rows = chunk;
   p.scale = scale;
   p.lb2 = static_cast<float>(lower_bound * kLog2e);
   p.anchor = kda_chunk_anchor(lower_bound, chunk);
-  const hipError_t e =
-      kda::launch_kda_fwd(p, static_cast<int>(D), chunk, vt, static_cast<hipStream_t>(stream));
+  const hipError_t e = kda::launch_kda_fwd(p, static_cast<int>(D), tile_rows(chunk), vt,
+                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

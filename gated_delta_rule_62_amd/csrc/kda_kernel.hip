@@ -25,8 +25,8 @@
 //      never formed: P^T = 2^Ca (Kc S^T) and O = 2^Ca (S Qc^T + U (2^-Ca Mqk)^T),
 //      the power of two applied to the fp32 results.
 //
-// Anchor.  The prefix of a chunk lies in [C b, 0] (b = lb log2(e)); the anchor is
-// its middle, Ca = C b / 2 (section 2's 16 b for 32-token chunks), so the centred
+// Anchor.  The prefix of a chunk of C tokens lies in [C b, 0] (b = lb log2(e)); the
+// anchor is its middle, Ca = C b / 2 (section 2's 16 b for 32-token chunks), so the centred
 // operands span 2^(Ca) .. 2^(-Ca) times a component of qh or kh, at most 2^118
 // for the spans the host admits, with as much room above the bf16 normal minimum
 // as below its maximum.  The state side runs 2^16 below scale: the accumulators
@@ -35,6 +35,12 @@
 // inside fp32 for state rows up to 2^25 in 1-norm; 2^(Ca + 16) restores P and
 // O, and the state is rescaled once on load and store.  The output scale is
 // applied with that factor rather than folded into qh.
+//
+// Short chunks.  A chunk may hold fewer tokens than the tile has rows (8, 4, 2 or
+// 1 in a 16-row tile): the empty rows are handled exactly like a ragged tail (zero
+// inputs, no decay, beta 0, no stores), and the decay span, hence the anchor, is
+// that of the tokens the chunk holds.  This admits strongly negative lower bounds
+// whose 16-token span would leave the bf16 window.
 //
 // Schedule.  Steps 1-5 only touch chunk-local data, step 6 is the strictly
 // ordered recurrence (section 3's scheduling property).  Waves 0..NSW-1 hold the
@@ -427,15 +433,18 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     s1 = s0 + p.T;
   }
   const int64_t H = p.H;
-  const int nchunks = (int)((s1 - s0 + C - 1) / C);
+  // Chunks of CR tokens; CR < C leaves the tile's last rows empty, which the ragged
+  // tail handling already covers (zero inputs, no decay, no stores).
+  const int CR = p.chunk_rows;
+  const int nchunks = (int)((s1 - s0 + CR - 1) / CR);
   const uint32_t row_bytes = (uint32_t)(H * D * 2);
   const float Ca = p.anchor;
   const float c1 = __builtin_amdgcn_exp2f(Ca + kStateExp);  // 2^(Ca + 16): restores P
   const float c1o = c1 * p.scale;                           // ... and O, with the scale
   const float c1i = __builtin_amdgcn_exp2f(-Ca);            // 2^-Ca
   auto chunk_valid = [&](int c) -> int {
-    const int64_t rem = s1 - (s0 + (int64_t)c * C);
-    return rem < C ? (int)rem : C;
+    const int64_t rem = s1 - (s0 + (int64_t)c * CR);
+    return rem < CR ? (int)rem : CR;
   };
 
   // ---- state: S^T accumulators of the state waves -----------------------------
@@ -659,7 +668,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   unsigned raw_b = 0;
   // g (gate waves), v and beta (job waves): consumed in phase A
   auto load_g = [&](int c) {
-    const int64_t tok_elem = ((s0 + (int64_t)c * C) * H + h) * D;
+    const int64_t tok_elem = ((s0 + (int64_t)c * CR) * H + h) * D;
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g + tok_elem, chunk_valid(c) * (int)row_bytes);
 #pragma unroll
     for (int ps = 0; ps < F::SPASS; ++ps)
@@ -669,7 +678,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
             rg, off_g + (uint32_t)i * row_bytes + 4u * F::CPG * ps, 0, 0);
   };
   auto load_vb = [&](int c) {
-    const int64_t cs = s0 + (int64_t)c * C;
+    const int64_t cs = s0 + (int64_t)c * CR;
     const int valid = chunk_valid(c);
     const int64_t tok_elem = (cs * H + h) * D;
     buf_load<F::EPV>(make_rsrc(p.v + tok_elem, valid * (int)row_bytes), off_v, raw_v);
@@ -678,7 +687,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   };
   // q and k: consumed in phase B
   auto load_qk = [&](int c) {
-    const int64_t cs = s0 + (int64_t)c * C;
+    const int64_t cs = s0 + (int64_t)c * CR;
     const int64_t tok_elem = (cs * H + h) * D;
     const int nb = chunk_valid(c) * (int)row_bytes;
     buf_load<F::EPT>(make_rsrc(p.q + tok_elem, nb), off_qk, raw_q);
@@ -927,7 +936,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
           }
           state_R(cur);
           lds_barrier();
-          state_B(cur, s0 + (int64_t)s * C, chunk_valid(s));
+          state_B(cur, s0 + (int64_t)s * CR, chunk_valid(s));
           if (more) {
             prep_B(nxt);
             load_qk(nxt2);
@@ -992,7 +1001,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
         if (is_state) state_R(cur);
         chunk_matrices(cur);
         lds_barrier();
-        if (is_state) state_B(cur, s0 + (int64_t)s * C, chunk_valid(s));
+        if (is_state) state_B(cur, s0 + (int64_t)s * CR, chunk_valid(s));
         if (more) {
           prep_B(nxt);
           load_qk(nxt2);

@@ -29,6 +29,8 @@ struct KdaParams {
   int32_t s_out_fp32;       // 1: final state is fp32
   int32_t s_kv;             // 1: states are [N, H, K, V] (key-major) instead of [N, H, V, K]
   int32_t n_vtiles;         // value tiles per (sequence, head)
+  int32_t chunk_rows;       // tokens per chunk: the tile height C, or fewer (1, 2, 4 or 8
+                            // in a 16-row tile) to narrow each chunk's decay span
   float scale;              // output scale
   float lb2;                // lower_bound * log2(e)
   float anchor;             // fixed base-2 exponent anchor of the chunk

@@ -15,8 +15,9 @@
  *     out_t = scale * S qh_t
  *
  * with qh, kh the L2-normalised q and k rows (x / sqrt(|x|^2 + 1e-6)).  The
- * library evaluates this in chunks of 16 or 32 tokens with bf16 matrix-core
- * products and an fp32 state that stays on chip for the whole sequence.
+ * library evaluates this in chunks of 32 or 16 tokens (fewer for strongly
+ * negative lower bounds) with bf16 matrix-core products and an fp32 state that
+ * stays on chip for the whole sequence.
  * Within a chunk the decayed operands are centred on a fixed exponent anchor
  * (section 2 of the PR #4262 summary); the state rows' 1-norms must stay below
  * 2^25 for the centred state products to stay inside fp32, and q and k rows
@@ -106,9 +107,12 @@ extern "C" {
  * kda_fwd_ordered for a caller-chosen order).
  *
  * Returns KDA_OK or a negative status.  The decay span of a chunk is
- * chunk * |lower_bound| * log2(e); it must not exceed 236 (|lb| <= 10.22 with
- * 16-token chunks).  The library uses 32-token chunks when their span allows it
- * (|lb| <= 5.112) and 16-token chunks otherwise; see kda_chunk_anchor.
+ * chunk * |lower_bound| * log2(e); it must not exceed 236.  The library uses the
+ * longest chunk whose span allows it: 32 tokens for |lb| <= 5.112, 16 for
+ * |lb| <= 10.22, then 8, 4, 2 and 1 token(s) per chunk up to |lb| <= 163.6
+ * (chunks shorter than 16 tokens run in 16-row tiles, so each halving of the
+ * chunk doubles the kernel's sequential steps).  A stronger lower bound returns
+ * KDA_ERR_BAD_LOWER_BOUND.  See kda_chunk_anchor.
  */
 int kda_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
             float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
@@ -118,8 +122,10 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
 
 /*
  * kda_fwd_sched -- kda_fwd with a forced schedule, for tests and tuning.
- *   chunk_size  0 (automatic), 16 or 32.  32 is rejected (KDA_ERR_BAD_LOWER_BOUND)
- *               when |lb| > 5.112.
+ *   chunk_size  0 (automatic), or tokens per chunk: 32, 16, 8, 4, 2 or 1
+ *               (KDA_ERR_BAD_SCHEDULE otherwise).  A chunk whose decay span
+ *               exceeds 236 (see kda_fwd) is rejected with
+ *               KDA_ERR_BAD_LOWER_BOUND, e.g. 32 when |lb| > 5.112.
  *   v_tile      0 (automatic) or the number of value rows one workgroup owns:
  *               a divisor of D that is a multiple of 16 and at least 32
  *               (KDA_ERR_BAD_SCHEDULE otherwise).  Automatic: D, or D/2 for

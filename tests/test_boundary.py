@@ -61,6 +61,8 @@ def test_anchor_window(lib):
     assert abs(kda.kda_chunk_anchor(-5.0, 32) - 16 * -5.0 * log2e) < 1e-4
     assert abs(kda.kda_chunk_anchor(-5.0, 32) + 115.4156) < 1e-3
     assert abs(kda.kda_chunk_anchor(-10.22, 16) + 117.96) < 1e-2
+    # one-token chunks at the strongest lower bound admitted: half of 163.5 log2(e)
+    assert abs(kda.kda_chunk_anchor(-163.5, 1) + 0.5 * 163.5 * log2e) < 1e-3
 
 
 # fake device addresses, far apart so that only deliberate overlaps overlap
@@ -139,17 +141,33 @@ def test_scalar_errors(lib):
         assert _check(lb=lb) == kda.KDA_ERR_BAD_LOWER_BOUND, lb
     assert _check(scale=float("nan")) == kda.KDA_ERR_BAD_SCALE
     # decay span chunk |lb| log2(e) <= 236: 32-token chunks to |lb| = 5.1118,
-    # 16-token chunks to 10.2236; the automatic schedule falls back to 16.
+    # 16-token chunks to 10.2236, then 8, 4, 2 and 1 token(s) per chunk up to
+    # |lb| = 236 / log2(e) = 163.58; the automatic schedule takes the longest chunk
+    # that fits and rejects only what one token's span cannot hold.
     assert _check(lb=-5.11, chunk=32) == kda.KDA_OK
     assert _check(lb=-5.12, chunk=32) == kda.KDA_ERR_BAD_LOWER_BOUND
     assert _check(lb=-5.12) == kda.KDA_OK
     assert _check(lb=-10.22) == kda.KDA_OK
-    assert _check(lb=-10.23) == kda.KDA_ERR_BAD_LOWER_BOUND
+    assert _check(lb=-10.23, chunk=16) == kda.KDA_ERR_BAD_LOWER_BOUND
+    limit = 236.0 / math.log2(math.e)
+    for rows in (32, 16, 8, 4, 2, 1):
+        inside, outside = -limit / rows * (1 - 1e-4), -limit / rows * (1 + 1e-4)
+        assert _check(lb=inside, chunk=rows) == kda.KDA_OK, rows
+        assert _check(lb=outside, chunk=rows) == kda.KDA_ERR_BAD_LOWER_BOUND, rows
+        assert _check(lb=inside) == kda.KDA_OK, rows
+    assert _check(lb=-163.5) == kda.KDA_OK
+    assert _check(lb=-163.7) == kda.KDA_ERR_BAD_LOWER_BOUND
+    assert _check(lb=-1e30) == kda.KDA_ERR_BAD_LOWER_BOUND
+    for rows in (3, 5, 12, 64, -1):
+        assert _check(chunk=rows) == kda.KDA_ERR_BAD_SCHEDULE, rows
 
 
 def test_schedule_errors(lib):
-    assert _check(chunk=8) == kda.KDA_ERR_BAD_SCHEDULE
+    assert _check(chunk=24) == kda.KDA_ERR_BAD_SCHEDULE
     assert _check(chunk=64) == kda.KDA_ERR_BAD_SCHEDULE
+    for rows in (8, 4, 2, 1):  # short chunks run in the 16-row tile's schedules
+        assert _check(chunk=rows) == kda.KDA_OK, rows
+        assert _check(chunk=rows, vt=64) == kda.KDA_OK, rows
     assert _check(vt=48) == kda.KDA_ERR_BAD_SCHEDULE
     assert _check(vt=16) == kda.KDA_ERR_BAD_SCHEDULE
     assert _check(D=32, vt=64) == kda.KDA_ERR_BAD_SCHEDULE

@@ -116,6 +116,23 @@ def test_varlen_edge_lengths_fp32_state(chunk):
         assert torch.equal(inp["final_state"][n], inp["initial_state"][n])
 
 
+@pytest.mark.parametrize("chunk", [8, 4, 2, 1])
+def test_short_chunks_forced(chunk):
+    """Chunks of 8, 4, 2 and 1 token(s) in a 16-row tile (the empty rows behave as a
+    ragged tail) at lb = -5: varlen edge lengths with fp32 states, and a ragged batch
+    at D = 64 and at D = 128 with the 64-row value tile."""
+    w = Workload("short_edges", B=1, T=0, H=2, D=128, seed=70 + chunk,
+                 lengths=[0, 1, 3, 8, 17, 0, 33], state_in="fp32", state_out="fp32")
+    inp = make_inputs(w, device=DEV)
+    _check_against_oracle(inp, chunk, tag="edges C%d" % chunk)
+    for n in (0, 5):
+        assert torch.equal(inp["final_state"][n], inp["initial_state"][n])
+    for D, vt in ((64, 0), (128, 64)):
+        w = Workload("short_ragged", B=2, T=45, H=2, D=D, seed=80 + chunk + D, state_in="bf16")
+        inp = make_inputs(w, device=DEV)
+        _check_against_oracle(inp, chunk, vt, tag="D%d C%d VT%d" % (D, chunk, vt))
+
+
 def test_max_head_count_at_the_offset_limit():
     """The largest H the host accepts at D = 32 (H * D * 2 * 32 just below 2^31: a chunk's
     byte offsets and buffer extents reach the 32-bit limit), ragged T = 40; the oracle
@@ -201,6 +218,22 @@ def test_saturated_gate_at_the_chunk_limits(lb):
     inp["g"].fill_(30.0)
     _check_against_oracle(inp, tag="saturated gate lb=%g" % lb)
     assert torch.isfinite(inp["out"].float()).all()
+
+
+@pytest.mark.parametrize("lb", [-15.0, -20.44, -40.88, -81.77, -163.5])
+def test_strong_lower_bounds_use_short_chunks(lb):
+    """Lower bounds past the 16-token limit (|lb| > 10.22): the library picks chunks of
+    8, 4, 2 or 1 token(s), each at the largest |lb| it admits except -15.  Random gates,
+    then every gate saturated (lambda = lb for every token and key: each chunk's decay
+    span fills the bf16 window)."""
+    for sat in (False, True):
+        w = Workload("short_lb", B=1, T=70, H=2, D=128, seed=31, lower_bound=lb,
+                     state_in="fp32", state_out="fp32")
+        inp = make_inputs(w, device=DEV)
+        if sat:
+            inp["g"].fill_(30.0)
+        _check_against_oracle(inp, tag="lb=%g%s" % (lb, " saturated" if sat else ""))
+        assert torch.isfinite(inp["out"].float()).all()
 
 
 def test_gate_and_beta_extremes_and_zero_or_huge_rows():
