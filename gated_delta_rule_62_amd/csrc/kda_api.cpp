@@ -47,12 +47,16 @@ bool chunk_rows_valid(int rows) {
 }
 int tile_rows(int rows) { return rows == 32 ? 32 : 16; }
 
-// The longest admissible chunk, or 0 when even one token's span is too wide
-// (|lb| above 236 / log2(e) = 163.6).
+// One-token chunks admit every lower bound: past |lb| = 236 / log2(e) = 163.6 the
+// kernel floors the per-token base-2 decay at -236 (a factor below 1e-71).
+bool rows_admissible(double lb, int rows) { return rows == 1 || chunk_admissible(lb, rows); }
+bool needs_decay_floor(double lb, int rows) { return rows == 1 && !chunk_admissible(lb, 1); }
+
+// The longest admissible chunk.
 int auto_chunk(double lb) {
-  for (int rows = 32; rows >= 1; rows /= 2)
+  for (int rows = 32; rows > 1; rows /= 2)
     if (chunk_admissible(lb, rows)) return rows;
-  return 0;
+  return 1;
 }
 
 // Compute units of the current device (256 on MI355X when the query fails, e.g.
@@ -104,13 +108,12 @@ int resolve(const void* q, const void* k, const void* v, const void* g, const vo
   if (!std::isfinite(scale)) return KDA_ERR_BAD_SCALE;
   if (!std::isfinite(lower_bound) || !(lower_bound < 0.f)) return KDA_ERR_BAD_LOWER_BOUND;
 
-  int chunk = chunk_size;
-  if (chunk == 0) {
-    chunk = auto_chunk(lower_bound);
-    if (chunk == 0) return KDA_ERR_BAD_LOWER_BOUND;
-  }
+  // lb log2(e) must be a finite fp32 value (|lb| below 2.35e38)
+  if (!std::isfinite(static_cast<float>(lower_bound * kLog2e))) return KDA_ERR_BAD_LOWER_BOUND;
+
+  int chunk = chunk_size == 0 ? auto_chunk(lower_bound) : chunk_size;
   if (!chunk_rows_valid(chunk)) return KDA_ERR_BAD_SCHEDULE;
-  if (!chunk_admissible(lower_bound, chunk)) return KDA_ERR_BAD_LOWER_BOUND;
+  if (!rows_admissible(lower_bound, chunk)) return KDA_ERR_BAD_LOWER_BOUND;
   const int tile = tile_rows(chunk);
   int vt = v_tile == 0 ? auto_v_tile(D, tile, num_seqs * H) : v_tile;
   if (!kda::kda_schedule_supported(static_cast<int>(D), tile, vt)) return KDA_ERR_BAD_SCHEDULE;
@@ -191,6 +194,8 @@ int launch(const void* q, const void* k, const void* v, const void* g, const voi
   p.chunk_rows = chunk;
   p.scale = scale;
   p.lb2 = static_cast<float>(lower_bound * kLog2e);
+  p.lam2_floor = needs_decay_floor(lower_bound, chunk) ? static_cast<float>(-kMaxSpan)
+                                                       : -INFINITY;
   p.anchor = kda_chunk_anchor(lower_bound, chunk);
   const hipError_t e = kda::launch_kda_fwd(p, static_cast<int>(D), tile_rows(chunk), vt,
                                            static_cast<hipStream_t>(stream));
@@ -270,7 +275,9 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
 }
 
 float kda_chunk_anchor(float lower_bound, int chunk_size) {
-  return static_cast<float>(-0.5 * chunk_span(lower_bound, chunk_size));
+  const double span = chunk_span(lower_bound, chunk_size);
+  // one-token chunks past the window floor the decay at the window's width
+  return static_cast<float>(-0.5 * (chunk_size == 1 && span > kMaxSpan ? kMaxSpan : span));
 }
 
 const char* kda_status_string(int status) {

@@ -40,7 +40,9 @@
 // 1 in a 16-row tile): the empty rows are handled exactly like a ragged tail (zero
 // inputs, no decay, beta 0, no stores), and the decay span, hence the anchor, is
 // that of the tokens the chunk holds.  This admits strongly negative lower bounds
-// whose 16-token span would leave the bf16 window.
+// whose 16-token span would leave the bf16 window.  Past |lb| log2(e) = 236 even one
+// token's decay can leave it; one-token chunks then floor the per-token base-2 decay
+// at -236, a factor below 1e-71, which changes no result representable in fp32.
 //
 // Schedule.  Steps 1-5 only touch chunk-local data, step 6 is the strictly
 // ordered recurrence (section 3's scheduling property).  Waves 0..NSW-1 hold the
@@ -734,13 +736,19 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       float t0 = 0.f, t1 = 0.f;
 #pragma unroll
       for (int i = 0; i < F::RPG; ++i) {
-        float lbv = p.lb2;
-        if constexpr (!decltype(full)::value)
-          lbv = g_row0 + i < nxt_valid ? p.lb2 : 0.f;  // no decay past the sequence
         const float z0 = __builtin_fmaf(bflo(raw_g[ps][i]), gate_mul, gate_add[ps][0]);
         const float z1 = __builtin_fmaf(bfhi(raw_g[ps][i]), gate_mul, gate_add[ps][1]);
-        t0 = __builtin_fmaf(lbv, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z0)), t0);
-        t1 = __builtin_fmaf(lbv, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z1)), t1);
+        if constexpr (decltype(full)::value) {
+          t0 = __builtin_fmaf(p.lb2, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z0)), t0);
+          t1 = __builtin_fmaf(p.lb2, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z1)), t1);
+        } else {
+          // no decay past the sequence; the floor only acts in one-token chunks
+          const float lbv = g_row0 + i < nxt_valid ? p.lb2 : 0.f;
+          t0 += __builtin_fmaxf(lbv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z0)),
+                                p.lam2_floor);
+          t1 += __builtin_fmaxf(lbv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z1)),
+                                p.lam2_floor);
+        }
         run0[i] = t0;
         run1[i] = t1;
       }

@@ -33,6 +33,8 @@ struct KdaParams {
                             // in a 16-row tile) to narrow each chunk's decay span
   float scale;              // output scale
   float lb2;                // lower_bound * log2(e)
+  float lam2_floor;         // smallest per-token base-2 decay kept (-236 in one-token chunks
+                            // when lb2 < -236, else -infinity: no floor)
   float anchor;             // fixed base-2 exponent anchor of the chunk
 };
 

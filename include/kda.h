@@ -57,8 +57,9 @@ extern "C" {
                                      /* num_seqs != B without cu_seqlens                 */
 #define KDA_ERR_BAD_ALIAS (-5)       /* an output overlaps an input or the other output; */
                                      /* only the exact in-place state alias is allowed   */
-#define KDA_ERR_BAD_LOWER_BOUND (-6) /* lower_bound not finite, not < 0, or too strong   */
-                                     /* for the chunk size (see kda_fwd)                 */
+#define KDA_ERR_BAD_LOWER_BOUND (-6) /* lower_bound not finite, not < 0, below -2.35e38 */
+                                     /* (lb log2(e) not a finite float), or too strong   */
+                                     /* for a forced chunk size (see kda_fwd)            */
 #define KDA_ERR_BAD_SCALE (-7)       /* scale not finite                                 */
 #define KDA_ERR_BAD_SCHEDULE (-8)    /* unsupported forced chunk size or value tile      */
 #define KDA_ERR_HIP (-9)             /* the HIP runtime reported an error at launch      */
@@ -109,10 +110,12 @@ extern "C" {
  * Returns KDA_OK or a negative status.  The decay span of a chunk is
  * chunk * |lower_bound| * log2(e); it must not exceed 236.  The library uses the
  * longest chunk whose span allows it: 32 tokens for |lb| <= 5.112, 16 for
- * |lb| <= 10.22, then 8, 4, 2 and 1 token(s) per chunk up to |lb| <= 163.6
- * (chunks shorter than 16 tokens run in 16-row tiles, so each halving of the
- * chunk doubles the kernel's sequential steps).  A stronger lower bound returns
- * KDA_ERR_BAD_LOWER_BOUND.  See kda_chunk_anchor.
+ * |lb| <= 10.22, then 8, 4 and 2 tokens, and one token per chunk for every
+ * stronger lower bound (chunks shorter than 16 tokens run in 16-row tiles, so each
+ * halving of the chunk doubles the kernel's sequential steps).  Past
+ * |lb| = 163.6 one token's decay can exceed the span: the kernel then floors each
+ * token's decay factor at 2^-236 (about 1e-71), which differs from the exact
+ * recurrence by less than 1e-71 times the state.  See kda_chunk_anchor.
  */
 int kda_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
             float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
@@ -123,9 +126,10 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
 /*
  * kda_fwd_sched -- kda_fwd with a forced schedule, for tests and tuning.
  *   chunk_size  0 (automatic), or tokens per chunk: 32, 16, 8, 4, 2 or 1
- *               (KDA_ERR_BAD_SCHEDULE otherwise).  A chunk whose decay span
- *               exceeds 236 (see kda_fwd) is rejected with
- *               KDA_ERR_BAD_LOWER_BOUND, e.g. 32 when |lb| > 5.112.
+ *               (KDA_ERR_BAD_SCHEDULE otherwise).  A chunk of 2 or more tokens
+ *               whose decay span exceeds 236 (see kda_fwd) is rejected with
+ *               KDA_ERR_BAD_LOWER_BOUND, e.g. 32 when |lb| > 5.112; one-token
+ *               chunks take every lower bound.
  *   v_tile      0 (automatic) or the number of value rows one workgroup owns:
  *               a divisor of D that is a multiple of 16 and at least 32
  *               (KDA_ERR_BAD_SCHEDULE otherwise).  Automatic: D, or D/2 for
@@ -210,7 +214,8 @@ int kda_fwd_check(const void* q, const void* k, const void* v, const void* g, co
 /*
  * kda_chunk_anchor -- the fixed exponent anchor Ca (base 2) the library centres a
  * chunk's operands on: the middle of the chunk's decay span,
- * chunk_size * lower_bound * log2(e) / 2.  For 32-token chunks this is section 2
+ * chunk_size * lower_bound * log2(e) / 2 (-118 for one-token chunks whose span
+ * exceeds 236, where the decay is floored).  For 32-token chunks this is section 2
  * of the PR #4262 summary's 16 * lower_bound * log2(e) (about -115.42 for
  * lower_bound = -5).  The centred operands then reach 2^(-Ca) at most and keep
  * as much room above the bf16 normal minimum as below its maximum, which the

@@ -61,8 +61,9 @@ def test_anchor_window(lib):
     assert abs(kda.kda_chunk_anchor(-5.0, 32) - 16 * -5.0 * log2e) < 1e-4
     assert abs(kda.kda_chunk_anchor(-5.0, 32) + 115.4156) < 1e-3
     assert abs(kda.kda_chunk_anchor(-10.22, 16) + 117.96) < 1e-2
-    # one-token chunks at the strongest lower bound admitted: half of 163.5 log2(e)
+    # one-token chunks: half the token's span, at most half the window (118)
     assert abs(kda.kda_chunk_anchor(-163.5, 1) + 0.5 * 163.5 * log2e) < 1e-3
+    assert kda.kda_chunk_anchor(-1e4, 1) == -118.0
 
 
 # fake device addresses, far apart so that only deliberate overlaps overlap
@@ -141,23 +142,27 @@ def test_scalar_errors(lib):
         assert _check(lb=lb) == kda.KDA_ERR_BAD_LOWER_BOUND, lb
     assert _check(scale=float("nan")) == kda.KDA_ERR_BAD_SCALE
     # decay span chunk |lb| log2(e) <= 236: 32-token chunks to |lb| = 5.1118,
-    # 16-token chunks to 10.2236, then 8, 4, 2 and 1 token(s) per chunk up to
-    # |lb| = 236 / log2(e) = 163.58; the automatic schedule takes the longest chunk
-    # that fits and rejects only what one token's span cannot hold.
+    # 16-token chunks to 10.2236, then 8, 4 and 2 tokens per chunk; one-token chunks
+    # take every lower bound whose lb log2(e) is a finite fp32 value (past 163.58 the
+    # kernel floors the per-token decay at 2^-236); the automatic schedule takes the
+    # longest chunk that fits.
     assert _check(lb=-5.11, chunk=32) == kda.KDA_OK
     assert _check(lb=-5.12, chunk=32) == kda.KDA_ERR_BAD_LOWER_BOUND
     assert _check(lb=-5.12) == kda.KDA_OK
     assert _check(lb=-10.22) == kda.KDA_OK
     assert _check(lb=-10.23, chunk=16) == kda.KDA_ERR_BAD_LOWER_BOUND
     limit = 236.0 / math.log2(math.e)
-    for rows in (32, 16, 8, 4, 2, 1):
+    for rows in (32, 16, 8, 4, 2):
         inside, outside = -limit / rows * (1 - 1e-4), -limit / rows * (1 + 1e-4)
         assert _check(lb=inside, chunk=rows) == kda.KDA_OK, rows
         assert _check(lb=outside, chunk=rows) == kda.KDA_ERR_BAD_LOWER_BOUND, rows
         assert _check(lb=inside) == kda.KDA_OK, rows
-    assert _check(lb=-163.5) == kda.KDA_OK
-    assert _check(lb=-163.7) == kda.KDA_ERR_BAD_LOWER_BOUND
-    assert _check(lb=-1e30) == kda.KDA_ERR_BAD_LOWER_BOUND
+        assert _check(lb=outside) == kda.KDA_OK, rows
+    for lb in (-163.5, -163.7, -1e4, -1e30, -2.3e38):
+        assert _check(lb=lb) == kda.KDA_OK, lb
+        assert _check(lb=lb, chunk=1) == kda.KDA_OK, lb
+        assert _check(lb=lb, chunk=2) == kda.KDA_ERR_BAD_LOWER_BOUND, lb
+    assert _check(lb=-2.4e38) == kda.KDA_ERR_BAD_LOWER_BOUND  # lb log2(e) overflows fp32
     for rows in (3, 5, 12, 64, -1):
         assert _check(chunk=rows) == kda.KDA_ERR_BAD_SCHEDULE, rows
 

@@ -220,12 +220,13 @@ def test_saturated_gate_at_the_chunk_limits(lb):
     assert torch.isfinite(inp["out"].float()).all()
 
 
-@pytest.mark.parametrize("lb", [-15.0, -20.44, -40.88, -81.77, -163.5])
+@pytest.mark.parametrize("lb", [-15.0, -20.44, -40.88, -81.77, -163.5, -200.0, -1e4, -1e30])
 def test_strong_lower_bounds_use_short_chunks(lb):
     """Lower bounds past the 16-token limit (|lb| > 10.22): the library picks chunks of
-    8, 4, 2 or 1 token(s), each at the largest |lb| it admits except -15.  Random gates,
-    then every gate saturated (lambda = lb for every token and key: each chunk's decay
-    span fills the bf16 window)."""
+    8, 4, 2 or 1 token(s), from -20.44 to -163.5 at the largest |lb| each admits, and
+    one-token chunks with the decay floored at 2^-236 beyond.  Random gates, then every
+    gate saturated (lambda = lb for every token and key: each chunk's decay span fills
+    the bf16 window, or the floor acts on every key)."""
     for sat in (False, True):
         w = Workload("short_lb", B=1, T=70, H=2, D=128, seed=31, lower_bound=lb,
                      state_in="fp32", state_out="fp32")
