@@ -387,8 +387,15 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   const int jtid = is_job ? tid - F::JOB_BASE * 64 : 0;  // thread index among them
 
   // ---- work item ---------------------------------------------------------
-  const int vt_idx = blockIdx.x % p.n_vtiles;
-  const int unit = blockIdx.x / p.n_vtiles;
+  // Workgroups go to the eight XCDs round-robin by index, so blocks x and x + 8
+  // share an XCD and its L2.  With several value tiles per (sequence, head), a
+  // group of 8 * n_vtiles blocks holds eight units and gives the tiles of each to
+  // blocks 8 apart: they read the same q, k and g, and the L2 serves all but the
+  // first read.  Blocks past the last unit (padding of the last group) exit.
+  const int grp = 8 * p.n_vtiles;
+  const int vt_idx = (int)(blockIdx.x % grp) / 8;
+  const int unit = (int)(blockIdx.x / grp) * 8 + (int)(blockIdx.x % 8);
+  if (unit >= p.N * p.H) return;  // uniform per workgroup
   const int h = unit % p.H;
   // Workgroups are dispatched in index order, so a caller's sequence order (for
   // example longest first) decides which sequences start first; it never changes
@@ -1023,7 +1030,9 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
 
 template <int D, int C, int VT, int NW, int NSW>
 hipError_t launch_one(const KdaParams& p, hipStream_t stream) {
-  const int64_t blocks = (int64_t)p.N * p.H * p.n_vtiles;
+  // one block per unit with one value tile; otherwise whole groups of eight units
+  const int64_t units = (int64_t)p.N * p.H;
+  const int64_t blocks = p.n_vtiles == 1 ? units : (units + 7) / 8 * 8 * p.n_vtiles;
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((kda_fwd_kernel<D, C, VT, NW, NSW>), dim3((unsigned)blocks), dim3(NW * 64), 0,
                      stream, p);
