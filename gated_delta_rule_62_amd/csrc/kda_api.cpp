@@ -289,8 +289,8 @@ const char* kda_status_string(int status) {
     case KDA_ERR_BAD_VARLEN: return "KDA_ERR_BAD_VARLEN: inconsistent cu_seqlens / num_seqs / B";
     case KDA_ERR_BAD_ALIAS: return "KDA_ERR_BAD_ALIAS: buffers overlap beyond the exact state alias";
     case KDA_ERR_BAD_LOWER_BOUND:
-      return "KDA_ERR_BAD_LOWER_BOUND: lower_bound must be finite, negative and inside the "
-             "chunk's bf16 exponent radius";
+      return "KDA_ERR_BAD_LOWER_BOUND: lower_bound must be finite, negative, above -2.35e38 "
+             "and, for a forced chunk of 2 or more tokens, inside its bf16 exponent radius";
     case KDA_ERR_BAD_SCALE: return "KDA_ERR_BAD_SCALE: scale must be finite";
     case KDA_ERR_BAD_SCHEDULE: return "KDA_ERR_BAD_SCHEDULE: unsupported chunk size or value tile";
     case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported an error";
