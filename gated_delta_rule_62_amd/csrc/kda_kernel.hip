@@ -208,6 +208,13 @@ __device__ constexpr int job_wave(int j) {
   return j & 1;
 }
 
+// One chunk of one (sequence, head): its first token, its valid rows and its head.
+struct Chunk {
+  int64_t tok;
+  int valid;
+  int h;
+};
+
 // Prepared operands of one chunk.
 template <class F>
 struct alignas(16) Slot {
@@ -455,74 +462,120 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     const int64_t rem = s1 - (s0 + (int64_t)c * CR);
     return rem < CR ? (int)rem : CR;
   };
+  auto ck = [&](int c) -> Chunk { return Chunk{s0 + (int64_t)c * CR, chunk_valid(c), h}; };
+  const int64_t sbase0 = ((int64_t)n * H + h) * D * D;
 
   // ---- state: S^T accumulators of the state waves -----------------------------
   // Loaded and stored only inside the state waves' code paths, so no other wave
   // keeps registers for it.
   const int wv0 = wave * 16 * F::NTW;          // first value column of a state wave (in the tile)
   const int vbase = vt_idx * VT + wv0;         // ... in the head
-  const int64_t sbase = ((int64_t)n * H + h) * D * D;
   f32x4_t S[F::KT][F::NTW];
-  auto state_in = [&]() {
+  // State I/O goes through a buffer descriptor based at the (sequence, head) state,
+  // with one lane offset and a per-tile constant in the instruction's scalar offset
+  // (no 64-bit address per tile).
+  // Lane l16 of group lg handles value vbase + 16 nt + l16 and keys
+  // key_of_row(16 kt + 4 lg) .. + 3 = 8 lg + kconst(kt) .. + 3.
+  auto kconst = [](int kt) { return 32 * (kt >> 1) + 4 * (kt & 1); };
+  // state_in issues the loads of the state's raw bits into the accumulators;
+  // state_cvt widens them (bf16) and applies the 2^-16 state scale.
+  auto state_in = [&](int64_t sbase) {
 #pragma unroll
     for (int kt = 0; kt < F::KT; ++kt)
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) S[kt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (p.s_in == nullptr) return;
-    // lane: value vbase + 16 nt + l16, four consecutive keys (one 8- or 16-byte
-    // access in the [V, K] layout; four element accesses, coalesced across the
-    // lanes' consecutive values, in the [K, V] layout)
+    const int es = p.s_in_fp32 ? 4 : 2;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(static_cast<const char*>(p.s_in) + sbase * es, D * D * es);
+    if (p.s_kv) {
+      // [K, V]: four element accesses per tile, coalesced across the lanes' values
+      const uint32_t lo = (uint32_t)((8 * lg * D + vbase + l16) * es);
+#pragma unroll
+      for (int kt = 0; kt < F::KT; ++kt)
+#pragma unroll
+        for (int nt = 0; nt < F::NTW; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = ((kconst(kt) + i) * D + 16 * nt) * es;
+            S[kt][nt][i] = p.s_in_fp32
+                               ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, lo, c, 0))
+                               : __uint_as_float(
+                                     (unsigned)__builtin_amdgcn_raw_buffer_load_b16(rs, lo, c, 0));
+          }
+      return;
+    }
+    // [V, K]: one 16-byte (fp32) or 8-byte (bf16) access per tile
+    const uint32_t lo = (uint32_t)(((vbase + l16) * D + 8 * lg) * es);
 #pragma unroll
     for (int kt = 0; kt < F::KT; ++kt)
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) {
-        const int64_t vrow = vbase + 16 * nt + l16;
-        const int64_t key0 = key_of_row(16 * kt + 4 * lg);
-        if (p.s_kv) {
-          const int64_t off = sbase + key0 * D + vrow;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            S[kt][nt][i] = kStateDown *
-                           (p.s_in_fp32 ? static_cast<const float*>(p.s_in)[off + i * D]
-                                        : bf2f(static_cast<const u16*>(p.s_in)[off + i * D]));
-          continue;
-        }
-        const int64_t off = sbase + vrow * D + key0;
+        const int c = (16 * nt * D + kconst(kt)) * es;
         if (p.s_in_fp32) {
-          S[kt][nt] = kStateDown *
-                      *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.s_in) + off);
+          S[kt][nt] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, lo, c, 0));
         } else {
-          const u32x2_t w =
-              *reinterpret_cast<const u32x2_t*>(static_cast<const u16*>(p.s_in) + off);
-          S[kt][nt] = kStateDown * f32x4_t{bflo(w[0]), bfhi(w[0]), bflo(w[1]), bfhi(w[1])};
+          const u32x2_t w = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, lo, c, 0));
+          S[kt][nt] = f32x4_t{__uint_as_float(w[0]), __uint_as_float(w[1]), 0.f, 0.f};
         }
       }
   };
-  auto state_out = [&]() {
-    if (p.s_out == nullptr) return;
+  auto state_cvt = [&]() {
+    if (p.s_in == nullptr) return;
 #pragma unroll
     for (int kt = 0; kt < F::KT; ++kt)
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) {
-        const int64_t vrow = vbase + 16 * nt + l16;
-        const int64_t key0 = key_of_row(16 * kt + 4 * lg);
-        const f32x4_t sv = kStateUp * S[kt][nt];
-        if (p.s_kv) {
-          const int64_t off = sbase + key0 * D + vrow;
+        const f32x4_t r = S[kt][nt];
+        if (p.s_in_fp32) {
+          S[kt][nt] = kStateDown * r;
+        } else if (p.s_kv) {
+          // one bf16 per element, in the low half of its word
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[kt][nt][i] = kStateDown * bflo(__float_as_uint(r[i]));
+        } else {
+          const unsigned w0 = __float_as_uint(r[0]), w1 = __float_as_uint(r[1]);
+          S[kt][nt] = kStateDown * f32x4_t{bflo(w0), bfhi(w0), bflo(w1), bfhi(w1)};
+        }
+      }
+  };
+  // The state is scaled back in place and stored tile by tile.
+  auto state_out = [&](int64_t sbase) {
+    if (p.s_out == nullptr) return;
+    const int es = p.s_out_fp32 ? 4 : 2;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(static_cast<char*>(p.s_out) + sbase * es, D * D * es);
+    if (p.s_kv) {
+      const uint32_t lo = (uint32_t)((8 * lg * D + vbase + l16) * es);
+#pragma unroll
+      for (int kt = 0; kt < F::KT; ++kt)
+#pragma unroll
+        for (int nt = 0; nt < F::NTW; ++nt) {
+          S[kt][nt] = kStateUp * S[kt][nt];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            if (p.s_out_fp32) static_cast<float*>(p.s_out)[off + i * D] = sv[i];
-            else static_cast<u16*>(p.s_out)[off + i * D] = to_bf16(sv[i]);
+            const int c = ((kconst(kt) + i) * D + 16 * nt) * es;
+            if (p.s_out_fp32)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[kt][nt][i]), rs, lo, c, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b16(to_bf16(S[kt][nt][i]), rs, lo, c, 0);
           }
-          continue;
         }
-        const int64_t off = sbase + vrow * D + key0;
-        if (p.s_out_fp32) {
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.s_out) + off) = sv;
-        } else {
-          *reinterpret_cast<u32x2_t*>(static_cast<u16*>(p.s_out) + off) =
-              u32x2_t{pack_bf16(sv[0], sv[1]), pack_bf16(sv[2], sv[3])};
-        }
+      return;
+    }
+    const uint32_t lo = (uint32_t)(((vbase + l16) * D + 8 * lg) * es);
+#pragma unroll
+    for (int kt = 0; kt < F::KT; ++kt)
+#pragma unroll
+      for (int nt = 0; nt < F::NTW; ++nt) {
+        S[kt][nt] = kStateUp * S[kt][nt];
+        const f32x4_t sv = S[kt][nt];
+        const int c = (16 * nt * D + kconst(kt)) * es;
+        if (p.s_out_fp32)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, sv), rs, lo, c, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b64(
+              u32x2_t{pack_bf16(sv[0], sv[1]), pack_bf16(sv[2], sv[3])}, rs, lo, c, 0);
       }
   };
 
@@ -589,7 +642,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   // formed; with the solve operands' power-of-two factors both halves come out
   // as U 2^-16, the state's own scale.  The output leaves as bf16 straight from
   // the accumulators, through a descriptor bounded to the chunk's valid rows.
-  auto state_B = [&](Slot<F>& cur, int64_t cur_start, int cur_valid) {
+  auto state_B = [&](Slot<F>& cur, const Chunk& ck) {
     u32x4_t bU[F::NTW];
     {
       const u32x4_t aX11 = lds_op_pad(&cur.SOL[l16][0], lg);
@@ -621,7 +674,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     // O = 2^Ca (O0' + U Mqk'^T), Mqk' = 2^-Ca Mqk: U as the A operand (value rows),
     // Mqk' rows as B (token columns)
     const __amdgpu_buffer_rsrc_t ro =
-        make_rsrc(p.out + (cur_start * H + h) * D + vt_idx * VT, cur_valid * (int)row_bytes);
+        make_rsrc(p.out + (ck.tok * H + ck.h) * D + vt_idx * VT, ck.valid * (int)row_bytes);
 #pragma unroll
     for (int ct = 0; ct < F::CT; ++ct) {
       u32x4_t bM;
@@ -654,14 +707,26 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   // Value row layout (job waves).
   const int v_row = jtid / F::TPRV;
   const int v_col = (jtid % F::TPRV) * F::EPV;
-  const float A = __expf(p.A_log[h]);
-  const float gate_mul = -A * kLog2e;  // sigmoid argument in base 2
-  float gate_add[F::SPASS][2];
+  // Gate parameters of the head: the sigmoid argument in base 2 is gate_mul g + gate_add.
+  float gate_mul, gate_add[F::SPASS][2];
+  float raw_alog, raw_dtb[F::SPASS][2];
+  auto load_gate_params = [&](int hh) {
+    raw_alog = p.A_log[hh];
 #pragma unroll
-  for (int ps = 0; ps < F::SPASS; ++ps)
+    for (int ps = 0; ps < F::SPASS; ++ps)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-      gate_add[ps][c] = gate_mul * p.dt_bias[(int64_t)h * D + g_col0 + 2 * F::CPG * ps + c];
+      for (int c = 0; c < 2; ++c)
+        raw_dtb[ps][c] = p.dt_bias[(int64_t)hh * D + g_col0 + 2 * F::CPG * ps + c];
+  };
+  auto set_gate_params = [&]() {
+    gate_mul = -__expf(raw_alog) * kLog2e;
+#pragma unroll
+    for (int ps = 0; ps < F::SPASS; ++ps)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) gate_add[ps][c] = gate_mul * raw_dtb[ps][c];
+  };
+  load_gate_params(h);
+  set_gate_params();
 
   // Raw inputs of the chunk to prepare next, in registers.  Buffer loads through a
   // descriptor bounded to the chunk's valid rows: rows past the end of the
@@ -676,9 +741,9 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   unsigned raw_g[F::SPASS][F::RPG];
   unsigned raw_b = 0;
   // g (gate waves), v and beta (job waves): consumed in phase A
-  auto load_g = [&](int c) {
-    const int64_t tok_elem = ((s0 + (int64_t)c * CR) * H + h) * D;
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g + tok_elem, chunk_valid(c) * (int)row_bytes);
+  auto load_g = [&](const Chunk& ck) {
+    const int64_t tok_elem = (ck.tok * H + ck.h) * D;
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g + tok_elem, ck.valid * (int)row_bytes);
 #pragma unroll
     for (int ps = 0; ps < F::SPASS; ++ps)
 #pragma unroll
@@ -686,19 +751,16 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
         raw_g[ps][i] = __builtin_amdgcn_raw_buffer_load_b32(
             rg, off_g + (uint32_t)i * row_bytes + 4u * F::CPG * ps, 0, 0);
   };
-  auto load_vb = [&](int c) {
-    const int64_t cs = s0 + (int64_t)c * CR;
-    const int valid = chunk_valid(c);
-    const int64_t tok_elem = (cs * H + h) * D;
-    buf_load<F::EPV>(make_rsrc(p.v + tok_elem, valid * (int)row_bytes), off_v, raw_v);
+  auto load_vb = [&](const Chunk& ck) {
+    const int64_t tok_elem = (ck.tok * H + ck.h) * D;
+    buf_load<F::EPV>(make_rsrc(p.v + tok_elem, ck.valid * (int)row_bytes), off_v, raw_v);
     raw_b = __builtin_amdgcn_raw_buffer_load_b16(
-        make_rsrc(p.beta + cs * H + h, valid * (int)H * 2), off_b, 0, 0);
+        make_rsrc(p.beta + ck.tok * H + ck.h, ck.valid * (int)H * 2), off_b, 0, 0);
   };
   // q and k: consumed in phase B
-  auto load_qk = [&](int c) {
-    const int64_t cs = s0 + (int64_t)c * CR;
-    const int64_t tok_elem = (cs * H + h) * D;
-    const int nb = chunk_valid(c) * (int)row_bytes;
+  auto load_qk = [&](const Chunk& ck) {
+    const int64_t tok_elem = (ck.tok * H + ck.h) * D;
+    const int nb = ck.valid * (int)row_bytes;
     buf_load<F::EPT>(make_rsrc(p.q + tok_elem, nb), off_qk, raw_q);
     buf_load<F::EPT>(make_rsrc(p.k + tok_elem, nb), off_qk, raw_k);
   };
@@ -929,15 +991,16 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   const int c1st = nchunks > 1 ? 1 : 0;
   if constexpr (F::SPLIT) {
     if (is_state) {
-      state_in();
+      state_in(sbase0);
+      state_cvt();
       if (nchunks > 0) {
-        load_g(0);
-        load_qk(0);
+        load_g(ck(0));
+        load_qk(ck(0));
         gate(sm.slot[0], chunk_valid(0));
-        load_g(c1st);
+        load_g(ck(c1st));
         lds_barrier();
         prep_B(sm.slot[0]);
-        load_qk(c1st);
+        load_qk(ck(c1st));
         lds_barrier();
         for (int s = 0; s < nchunks; ++s) {
           Slot<F>& cur = sm.slot[s & 1];
@@ -947,27 +1010,27 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
           state_A(cur);
           if (more) {
             gate(nxt, chunk_valid(s + 1));
-            load_g(nxt2);
+            load_g(ck(nxt2));
           }
           state_R(cur);
           lds_barrier();
-          state_B(cur, s0 + (int64_t)s * CR, chunk_valid(s));
+          state_B(cur, ck(s));
           if (more) {
             prep_B(nxt);
-            load_qk(nxt2);
+            load_qk(ck(nxt2));
           }
           lds_barrier();
         }
       }
-      state_out();
+      state_out(sbase0);
     } else if (nchunks > 0) {
-      load_vb(0);
-      load_qk(0);
+      load_vb(ck(0));
+      load_qk(ck(0));
       stage_vb(sm.slot[0], chunk_valid(0));
-      load_vb(c1st);
+      load_vb(ck(c1st));
       lds_barrier();
       prep_B(sm.slot[0]);
-      load_qk(c1st);
+      load_qk(ck(c1st));
       lds_barrier();
       for (int s = 0; s < nchunks; ++s) {
         Slot<F>& cur = sm.slot[s & 1];
@@ -976,30 +1039,33 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
         const int nxt2 = s + 2 < nchunks ? s + 2 : nchunks - 1;
         if (more) {
           stage_vb(nxt, chunk_valid(s + 1));
-          load_vb(nxt2);
+          load_vb(ck(nxt2));
         }
         chunk_matrices(cur);
         lds_barrier();
         if (more) {
           prep_B(nxt);
-          load_qk(nxt2);
+          load_qk(ck(nxt2));
         }
         lds_barrier();
       }
     }
   } else {
-    if (is_state) state_in();
+    if (is_state) {
+      state_in(sbase0);
+      state_cvt();
+    }
     if (nchunks > 0) {
-      load_g(0);
-      load_vb(0);
-      load_qk(0);
+      load_g(ck(0));
+      load_vb(ck(0));
+      load_qk(ck(0));
       gate(sm.slot[0], chunk_valid(0));
       stage_vb(sm.slot[0], chunk_valid(0));
-      load_g(c1st);
-      load_vb(c1st);
+      load_g(ck(c1st));
+      load_vb(ck(c1st));
       lds_barrier();
       prep_B(sm.slot[0]);
-      load_qk(c1st);
+      load_qk(ck(c1st));
       lds_barrier();
       for (int s = 0; s < nchunks; ++s) {
         Slot<F>& cur = sm.slot[s & 1];
@@ -1010,21 +1076,21 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
         if (more) {
           gate(nxt, chunk_valid(s + 1));
           stage_vb(nxt, chunk_valid(s + 1));
-          load_g(nxt2);
-          load_vb(nxt2);
+          load_g(ck(nxt2));
+          load_vb(ck(nxt2));
         }
         if (is_state) state_R(cur);
         chunk_matrices(cur);
         lds_barrier();
-        if (is_state) state_B(cur, s0 + (int64_t)s * CR, chunk_valid(s));
+        if (is_state) state_B(cur, ck(s));
         if (more) {
           prep_B(nxt);
-          load_qk(nxt2);
+          load_qk(ck(nxt2));
         }
         lds_barrier();
       }
     }
-    if (is_state) state_out();
+    if (is_state) state_out(sbase0);
   }
 }
 
