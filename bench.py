@@ -74,6 +74,23 @@ def measured_traffic(workload: str):
     return float(m_bytes.group(1))
 
 
+def gpu_clocks():
+    """The GPU's current shader (sclk) and memory (mclk) clocks as rocm-smi reports them, or
+    None when the tool is not usable."""
+    import subprocess
+    try:
+        res = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                             timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    found = {}
+    for line in res.stdout.splitlines():
+        m = re.search(r"\b(sclk|mclk)\b.*?\(([0-9.]+\s*[MG]hz)\)", line, flags=re.I)
+        if m and m.group(1).lower() not in found:
+            found[m.group(1).lower()] = m.group(2)
+    return found or None
+
+
 def cpu_baseline(inp, min_wall: float):
     """Times the fp64 oracle (the test suite's reference, unchanged) on the same
     workload on the host cores: whole runs repeated until min_wall seconds passed."""
@@ -240,6 +257,7 @@ def main():
         cold = timed_after(lambda: flush.sum())
         cold_dirty = timed_after(lambda: flush.fill_(1))
         del flush
+    clocks = gpu_clocks()  # after the timed launches, while the clocks are still up
     tokens = B * T
     value = tokens * args.steps / wall
 
@@ -274,6 +292,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
                      "algorithmic_bytes": nbytes, "counted_tflops": tflops},
         "kernel_source_hash": kernel_source_hash(),
+        "gpu_clocks": clocks,
     }
     if cold is not None:
         med = cold[len(cold) // 2]
