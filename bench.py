@@ -285,6 +285,10 @@ def main():
                    "chunk": chunk or "auto", "v_tile": args.v_tile or "auto",
                    "sequence_order": "longest first" if order is not None else "index"},
         "mfma_pct_of_bf16_peak": 100.0 * tflops / MFMA_BF16_PEAK_TFLOPS,
+        # the most any kernel could reach: counted FLOP over the time the algorithmic bytes
+        # take at the full HBM bandwidth
+        "mfma_pct_ceiling_at_hbm_peak":
+            100.0 * flops / (nbytes / (HBM_PEAK_GBS * 1e9)) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         "kernel_ms": ms_per_launch,
         "kernel_ms_median": singles[len(singles) // 2],
         "kernel_ms_min": singles[0],
