@@ -505,19 +505,26 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
           }
       return;
     }
-    // [V, K]: one 16-byte (fp32) or 8-byte (bf16) access per tile
+    // [V, K]: 16-byte accesses.  The two tiles of a 32-row step hold keys 8 lg + 32 ks
+    // .. + 3 and + 4 .. + 7 (the row order above), so in bf16 one access serves both.
     const uint32_t lo = (uint32_t)(((vbase + l16) * D + 8 * lg) * es);
+    if (p.s_in_fp32) {
 #pragma unroll
-    for (int kt = 0; kt < F::KT; ++kt)
+      for (int kt = 0; kt < F::KT; ++kt)
+#pragma unroll
+        for (int nt = 0; nt < F::NTW; ++nt)
+          S[kt][nt] = __builtin_bit_cast(
+              f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, lo, (16 * nt * D + kconst(kt)) * 4, 0));
+      return;
+    }
+#pragma unroll
+    for (int ks = 0; ks < F::KS; ++ks)
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) {
-        const int c = (16 * nt * D + kconst(kt)) * es;
-        if (p.s_in_fp32) {
-          S[kt][nt] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, lo, c, 0));
-        } else {
-          const u32x2_t w = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, lo, c, 0));
-          S[kt][nt] = f32x4_t{__uint_as_float(w[0]), __uint_as_float(w[1]), 0.f, 0.f};
-        }
+        const u32x4_t w = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, lo, (16 * nt * D + 32 * ks) * 2, 0));
+        S[2 * ks][nt] = f32x4_t{__uint_as_float(w[0]), __uint_as_float(w[1]), 0.f, 0.f};
+        S[2 * ks + 1][nt] = f32x4_t{__uint_as_float(w[2]), __uint_as_float(w[3]), 0.f, 0.f};
       }
   };
   auto state_cvt = [&]() {
@@ -564,18 +571,27 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       return;
     }
     const uint32_t lo = (uint32_t)(((vbase + l16) * D + 8 * lg) * es);
+    if (p.s_out_fp32) {
 #pragma unroll
-    for (int kt = 0; kt < F::KT; ++kt)
+      for (int kt = 0; kt < F::KT; ++kt)
+#pragma unroll
+        for (int nt = 0; nt < F::NTW; ++nt) {
+          S[kt][nt] = kStateUp * S[kt][nt];
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, S[kt][nt]), rs, lo,
+                                                 (16 * nt * D + kconst(kt)) * 4, 0);
+        }
+      return;
+    }
+    // bf16: one 16-byte store per tile pair (see state_in)
+#pragma unroll
+    for (int ks = 0; ks < F::KS; ++ks)
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) {
-        S[kt][nt] = kStateUp * S[kt][nt];
-        const f32x4_t sv = S[kt][nt];
-        const int c = (16 * nt * D + kconst(kt)) * es;
-        if (p.s_out_fp32)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, sv), rs, lo, c, 0);
-        else
-          __builtin_amdgcn_raw_buffer_store_b64(
-              u32x2_t{pack_bf16(sv[0], sv[1]), pack_bf16(sv[2], sv[3])}, rs, lo, c, 0);
+        const f32x4_t a0 = kStateUp * S[2 * ks][nt], a1 = kStateUp * S[2 * ks + 1][nt];
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4_t{pack_bf16(a0[0], a0[1]), pack_bf16(a0[2], a0[3]), pack_bf16(a1[0], a1[1]),
+                    pack_bf16(a1[2], a1[3])},
+            rs, lo, (16 * nt * D + 32 * ks) * 2, 0);
       }
   };
 
