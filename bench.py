@@ -75,19 +75,26 @@ def measured_traffic(workload: str):
 
 
 def gpu_clocks():
-    """The GPU's current shader (sclk) and memory (mclk) clocks as rocm-smi reports them, or
-    None when the tool is not usable."""
-    import subprocess
+    """The GPU's current shader (sclk) and memory (mclk) clock levels, read from the amdgpu
+    driver's sysfs files of this device (the ones rocm-smi reports), or None when they are
+    not readable.  No other program is started."""
+    import torch
     try:
-        res = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
-                             timeout=20)
-    except (OSError, subprocess.SubprocessError):
+        pr = torch.cuda.get_device_properties(torch.cuda.current_device())
+        dev = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (pr.pci_domain_id, pr.pci_bus_id,
+                                                         pr.pci_device_id)
+    except (AttributeError, RuntimeError):
         return None
     found = {}
-    for line in res.stdout.splitlines():
-        m = re.search(r"\b(sclk|mclk)\b.*?\(([0-9.]+\s*[MG]hz)\)", line, flags=re.I)
-        if m and m.group(1).lower() not in found:
-            found[m.group(1).lower()] = m.group(2)
+    for name in ("sclk", "mclk"):
+        try:
+            text = open(os.path.join(dev, "pp_dpm_" + name)).read()
+        except OSError:
+            continue
+        for line in text.splitlines():
+            m = re.search(r"([0-9.]+\s*[MG]hz)\s*\*\s*$", line, flags=re.I)
+            if m:
+                found[name] = m.group(1)
     return found or None
 
 
@@ -150,6 +157,9 @@ def main():
     ap.add_argument("--workload", default="batched")
     ap.add_argument("--chunk", type=int, default=None, help="force the chunk size")
     ap.add_argument("--v-tile", type=int, default=0, help="force the value tile")
+    ap.add_argument("--path", choices=("fused", "split"), default="fused",
+                    help="fused: the one-kernel forward (kda_fwd_sched); split: the prep and "
+                         "recurrent kernels with a workspace (kda_fwd_split), both timed")
     ap.add_argument("--longest-first", action="store_true",
                     help="packed workloads: dispatch sequences longest first (kda_fwd_ordered); "
                          "the order is computed once, before the timed launches")
@@ -196,7 +206,15 @@ def main():
     args_c = kda.c_args(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"],
                         inp["out"], inp["A_log"], inp["dt_bias"], inp["lower_bound"],
                         inp["initial_state"], inp["final_state"], inp["cu_seqlens"], stream)
-    if order is not None:
+    if args.path == "split":
+        if order is not None or args.chunk is not None or w.chunk_size:
+            print("--path split takes the automatic chunk length and the index order",
+                  file=sys.stderr)
+            sys.exit(2)
+        ws_bytes = kda.kda_split_workspace_bytes(B * T, args_c[15], H, D, w.lower_bound, 0)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        call = lambda: lib.kda_fwd_split(*args_c, ws.data_ptr(), ws_bytes, int(args.v_tile))
+    elif order is not None:
         call = lambda: lib.kda_fwd_ordered(*args_c, order.data_ptr())
     else:
         call = lambda: lib.kda_fwd_sched(*args_c, int(chunk), int(args.v_tile))
@@ -283,7 +301,8 @@ def main():
                                    w.name, B, T, H, D, w.lower_bound, w.state_in, w.state_out),
                    "B": B, "T": T, "H": H, "D": D, "token_heads": token_heads(inp),
                    "chunk": chunk or "auto", "v_tile": args.v_tile or "auto",
-                   "sequence_order": "longest first" if order is not None else "index"},
+                   "sequence_order": "longest first" if order is not None else "index",
+                   "path": args.path},
         "mfma_pct_of_bf16_peak": 100.0 * tflops / MFMA_BF16_PEAK_TFLOPS,
         # the most any kernel could reach: counted FLOP over the time the algorithmic bytes
         # take at the full HBM bandwidth
@@ -293,7 +312,8 @@ def main():
         "kernel_ms_median": singles[len(singles) // 2],
         "kernel_ms_min": singles[0],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(w.name) if args.path == "fused" else None,
                      "algorithmic_bytes": nbytes, "counted_tflops": tflops},
         "kernel_source_hash": kernel_source_hash(),
         "gpu_clocks": clocks,

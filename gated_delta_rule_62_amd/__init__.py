@@ -14,6 +14,7 @@ import os
 from ._build import LIB_PATH, build  # noqa: F401  (build() is the in-tree compile step)
 
 __all__ = ["kda_fwd", "kda_fwd_sched", "kda_fwd_ordered", "kda_fwd_transposed_state",
+           "kda_fwd_split", "kda_split_workspace_bytes",
            "kda_longest_first", "kda_fwd_check", "c_args",
            "kda_chunk_anchor", "kda_status_string", "KdaError", "library_path", "load_library"]
 
@@ -27,6 +28,7 @@ KDA_ERR_BAD_LOWER_BOUND = -6
 KDA_ERR_BAD_SCALE = -7
 KDA_ERR_BAD_SCHEDULE = -8
 KDA_ERR_HIP = -9
+KDA_ERR_BAD_WORKSPACE = -10
 KDA_DTYPE_BF16 = 0
 KDA_DTYPE_FP32 = 1
 
@@ -67,6 +69,10 @@ def load_library():
     lib.kda_fwd_transposed_state.restype = i32
     lib.kda_longest_first.argtypes = [vp, i64, vp, vp]
     lib.kda_longest_first.restype = i32
+    lib.kda_split_workspace_bytes.argtypes = [i64, i64, i64, i64, f32, i32]
+    lib.kda_split_workspace_bytes.restype = i64
+    lib.kda_fwd_split.argtypes = common + [vp, vp, i64, i32]
+    lib.kda_fwd_split.restype = i32
     lib.kda_fwd_check.argtypes = common + [i32, i32]
     lib.kda_fwd_check.restype = i32
     lib.kda_chunk_anchor.argtypes = [f32, i32]
@@ -202,6 +208,36 @@ def kda_fwd_transposed_state(q, k, v, g, beta, scale, out, A_log, dt_bias, lower
                   final_state, cu_seqlens, stream)
     with _on_device(q):
         st = load_library().kda_fwd_transposed_state(*args)
+    if st != KDA_OK:
+        raise KdaError(st)
+
+
+def kda_split_workspace_bytes(T_total: int, num_seqs: int, H: int, D: int, lower_bound: float,
+                              chunk_size: int = 0) -> int:
+    """Bytes of the workspace ``kda_fwd_split`` needs (raises KdaError when the split
+    does not run these sizes)."""
+    n = load_library().kda_split_workspace_bytes(int(T_total), int(num_seqs), int(H), int(D),
+                                                 float(lower_bound), int(chunk_size))
+    if n < 0:
+        raise KdaError(int(n))
+    return int(n)
+
+
+def kda_fwd_split(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, workspace,
+                  initial_state=None, final_state=None, cu_seqlens=None, v_tile: int = 0,
+                  stream=None) -> None:
+    """``kda_fwd`` as two kernels: a token-parallel preparation of every chunk into
+    ``workspace`` (a contiguous uint8 device tensor of at least ``kda_split_workspace_bytes``
+    bytes), then the recurrent kernel on value tiles of ``v_tile`` rows (0: automatic).
+    The results are bitwise those of ``kda_fwd_sched`` with the same value tile."""
+    import torch
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-d uint8 tensor")
+    args = c_args(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                  final_state, cu_seqlens, stream, extra=(workspace,))
+    with _on_device(q):
+        st = load_library().kda_fwd_split(*args, workspace.data_ptr(), workspace.numel(),
+                                          int(v_tile))
     if st != KDA_OK:
         raise KdaError(st)
 

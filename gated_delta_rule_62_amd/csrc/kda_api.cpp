@@ -146,19 +146,55 @@ int resolve(const void* q, const void* k, const void* v, const void* g, const vo
   return KDA_OK;
 }
 
-// Validates, fills the launch parameters and enqueues the kernel.
+// Bytes of the split's workspace per head for a resolved chunk length, or a negative
+// status: the split runs D = 128 only, and every record offset and the prep grid
+// must fit 31 bits.
+int64_t split_head_bytes(int64_t T_total, int64_t num_seqs, int64_t H, int64_t D, int chunk) {
+  if (D != 128) return KDA_ERR_BAD_SCHEDULE;
+  const int64_t slots = kda::kda_split_slots(T_total, num_seqs, chunk);
+  const int64_t rec = kda::kda_record_bytes(D, tile_rows(chunk));
+  if (slots > (((int64_t)1 << 31) - 1) / rec || slots > (((int64_t)1 << 31) - 1) / H)
+    return KDA_ERR_BAD_SHAPE;
+  return slots * rec;
+}
+
+// Validates, fills the launch parameters and enqueues the kernel, or with a
+// workspace (split) the prep and recurrent kernels.
 int launch(const void* q, const void* k, const void* v, const void* g, const void* beta,
            float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
            const void* initial_state, int initial_state_dtype, void* final_state,
            int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B,
            int64_t T, int64_t H, int64_t D, void* stream, int chunk_size, int v_tile,
-           const int32_t* seq_order, int state_kv) {
+           const int32_t* seq_order, int state_kv, bool split = false, void* workspace = nullptr,
+           int64_t workspace_bytes = 0) {
   int chunk = 0, vt = 0;
   const int st = resolve(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
                          initial_state, initial_state_dtype, final_state, final_state_dtype,
                          cu_seqlens, num_seqs, B, T, H, D, chunk_size, v_tile, seq_order, &chunk,
                          &vt);
   if (st != KDA_OK) return st;
+  int64_t head_bytes = 0;
+  if (split) {
+    if (!kda::kda_split_supported(static_cast<int>(D), tile_rows(chunk), vt))
+      return KDA_ERR_BAD_SCHEDULE;
+    head_bytes = split_head_bytes(B * T, num_seqs, H, D, chunk);
+    if (head_bytes < 0) return static_cast<int>(head_bytes);
+    if (!workspace) return KDA_ERR_NULL_ARG;
+    if (workspace_bytes < head_bytes * H) return KDA_ERR_BAD_WORKSPACE;
+    // the workspace is written: it must not overlap any argument buffer
+    const int64_t act = B * T * H * D * 2;
+    const int64_t st_elems = num_seqs * H * D * D;
+    const Range rw = make_range(workspace, head_bytes * H);
+    const Range others[] = {
+        make_range(q, act), make_range(k, act), make_range(v, act), make_range(g, act),
+        make_range(beta, B * T * H * 2), make_range(A_log, H * 4), make_range(dt_bias, H * D * 4),
+        make_range(cu_seqlens, cu_seqlens ? (num_seqs + 1) * 8 : 0), make_range(out, act),
+        make_range(initial_state, initial_state ? st_elems * (initial_state_dtype ? 4 : 2) : 0),
+        make_range(final_state, final_state ? st_elems * (final_state_dtype ? 4 : 2) : 0)};
+    for (const Range& r : others) {
+      if (overlaps(rw, r)) return KDA_ERR_BAD_ALIAS;
+    }
+  }
 
   kda::KdaParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -197,8 +233,13 @@ int launch(const void* q, const void* k, const void* v, const void* g, const voi
   p.lam2_floor = needs_decay_floor(lower_bound, chunk) ? static_cast<float>(-kMaxSpan)
                                                        : -INFINITY;
   p.anchor = kda_chunk_anchor(lower_bound, chunk);
-  const hipError_t e = kda::launch_kda_fwd(p, static_cast<int>(D), tile_rows(chunk), vt,
-                                           static_cast<hipStream_t>(stream));
+  p.ws = workspace;
+  p.ws_head_bytes = head_bytes;
+  const hipError_t e =
+      split ? kda::launch_kda_split(p, static_cast<int>(D), tile_rows(chunk), vt,
+                                    static_cast<hipStream_t>(stream))
+            : kda::launch_kda_fwd(p, static_cast<int>(D), tile_rows(chunk), vt,
+                                  static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -274,6 +315,30 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
                        B, T, H, D, stream, 0, 0);
 }
 
+int64_t kda_split_workspace_bytes(int64_t T_total, int64_t num_seqs, int64_t H, int64_t D,
+                                  float lower_bound, int chunk_size) {
+  if (T_total < 0 || num_seqs < 1 || H < 1) return KDA_ERR_BAD_SHAPE;
+  if (!std::isfinite(lower_bound) || !(lower_bound < 0.f) ||
+      !std::isfinite(static_cast<float>(lower_bound * kLog2e)))
+    return KDA_ERR_BAD_LOWER_BOUND;
+  const int chunk = chunk_size == 0 ? auto_chunk(lower_bound) : chunk_size;
+  if (!chunk_rows_valid(chunk)) return KDA_ERR_BAD_SCHEDULE;
+  if (!rows_admissible(lower_bound, chunk)) return KDA_ERR_BAD_LOWER_BOUND;
+  const int64_t head_bytes = split_head_bytes(T_total, num_seqs, H, D, chunk);
+  return head_bytes < 0 ? head_bytes : head_bytes * H;
+}
+
+int kda_fwd_split(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                  float scale, void* out, const float* A_log, const float* dt_bias,
+                  float lower_bound, const void* initial_state, int initial_state_dtype,
+                  void* final_state, int final_state_dtype, const int64_t* cu_seqlens,
+                  int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t D, void* stream,
+                  void* workspace, int64_t workspace_bytes, int v_tile) {
+  return launch(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T,
+                H, D, stream, 0, v_tile, nullptr, 0, true, workspace, workspace_bytes);
+}
+
 float kda_chunk_anchor(float lower_bound, int chunk_size) {
   const double span = chunk_span(lower_bound, chunk_size);
   // one-token chunks past the window floor the decay at the window's width
@@ -294,6 +359,8 @@ const char* kda_status_string(int status) {
     case KDA_ERR_BAD_SCALE: return "KDA_ERR_BAD_SCALE: scale must be finite";
     case KDA_ERR_BAD_SCHEDULE: return "KDA_ERR_BAD_SCHEDULE: unsupported chunk size or value tile";
     case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported an error";
+    case KDA_ERR_BAD_WORKSPACE:
+      return "KDA_ERR_BAD_WORKSPACE: the workspace is smaller than kda_split_workspace_bytes";
     default: return "KDA_ERR_UNKNOWN";
   }
 }

@@ -1,5 +1,13 @@
 // Fused KDA recurrent prefill forward for gfx950 (CDNA4).
 //
+// The same kernel template also runs the two halves of the two-kernel split
+// (FlashKDA's prep and recurrent kernels as the FlashInfer PR #4262 summary
+// describes them): a token-parallel kernel that prepares one chunk of one head per
+// workgroup and stores what the state side reads as a workspace record, and a
+// recurrent kernel that copies the records back into LDS instead of preparing the
+// chunks.  Both run this file's own preparation and state-side code, so the split
+// gives the fused kernel's results bit for bit.
+//
 // One workgroup owns one (sequence n, head h, value tile j) work item and walks
 // that sequence's chunks in order.  The fp32 state stays in MFMA accumulator
 // registers for the whole sequence (the FlashInfer PR #4262 summary keeps it
@@ -227,9 +235,9 @@ struct alignas(16) Slot {
   float beta[F::C];          // sigmoid(beta), zero past the sequence
 };
 
-template <class F>
+template <class F, int NSLOT>
 struct alignas(16) Smem {
-  Slot<F> slot[2];
+  Slot<F> slot[NSLOT];       // two alternate in the chunk loop; the prep kernel uses one
   u16 Qc[F::C][F::LDQ];      // centred operands (key order) of the chunk whose state side,
                              // matrices and preparation alternate in them
   u16 Kc[F::C][F::LDQ];
@@ -378,10 +386,19 @@ __device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off,
   }
 }
 
-template <int D, int C, int VT, int NW, int NSW>
+// Kernel modes: the fused forward; the split's token-parallel preparation (one
+// chunk of one head per workgroup, written to the workspace as a record); the
+// split's recurrent side (the fused schedule with every record read back instead
+// of prepared).
+constexpr int kModeFused = 0;
+constexpr int kModePrep = 1;
+constexpr int kModeRecur = 2;
+
+template <int D, int C, int VT, int NW, int NSW, int MODE>
 __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   using F = Cfg<D, C, VT, NW, NSW>;
-  __shared__ Smem<F> sm;
+  static_assert(MODE == kModeFused || F::SPLIT, "the split runs the role-split schedules only");
+  __shared__ Smem<F, MODE == kModePrep ? 1 : 2> sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -393,60 +410,95 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   const int jw = is_job ? wave - F::JOB_BASE : 0;        // index among the job waves
   const int jtid = is_job ? tid - F::JOB_BASE * 64 : 0;  // thread index among them
 
-  // ---- work item ---------------------------------------------------------
+  // ---- work item (fused and recurrent kernels; the prep kernel maps slots) ---
   // Workgroups go to the eight XCDs round-robin by index, so blocks x and x + 8
   // share an XCD and its L2.  With several value tiles per (sequence, head), a
   // group of 8 * n_vtiles blocks holds eight units and gives the tiles of each to
   // blocks 8 apart: they read the same q, k and g, and the L2 serves all but the
   // first read.  Blocks past the last unit (padding of the last group) exit.
-  const int grp = 8 * p.n_vtiles;
-  const int vt_idx = (int)(blockIdx.x % grp) / 8;
-  const int unit = (int)(blockIdx.x / grp) * 8 + (int)(blockIdx.x % 8);
-  if (unit >= p.N * p.H) return;  // uniform per workgroup
-  const int h = unit % p.H;
-  // Workgroups are dispatched in index order, so a caller's sequence order (for
-  // example longest first) decides which sequences start first; it never changes
-  // what a workgroup computes.  Entries are clamped into [0, N).
-  int n = unit / p.H;
-  if (p.order != nullptr) {
-    const int o = p.order[n];
-    n = o < 0 ? 0 : (o >= p.N ? p.N - 1 : o);
-  } else if (p.auto_order) {  // uniform
-    // Longest first without a caller order (packed batches of at most
-    // kMaxAutoOrderSeqs sequences whose workgroups outnumber the CUs): every
-    // workgroup ranks the lengths, ties by index, and takes the sequence whose rank
-    // is its slot.  Eight lanes share a candidate and sum its rank over their
-    // share of the others; the prefix tile, not in use yet, holds the lengths.
-    int* lens = reinterpret_cast<int*>(&sm.G[0][0]);
-    for (int i = tid; i < p.N; i += F::NTHR) {
-      const int64_t l = p.cu[i + 1] - p.cu[i];
-      lens[i] = l < 0 ? 0 : (l > 0x7fffffff ? 0x7fffffff : (int)l);
+  // Start and end of sequence nn, clamped into [0, T_total].
+  auto seq_bounds = [&](int nn, int64_t& a, int64_t& b) {
+    if (p.cu != nullptr) {
+      a = p.cu[nn];
+      b = p.cu[nn + 1];
+      a = a < 0 ? 0 : (a > p.T_total ? p.T_total : a);
+      b = b < a ? a : (b > p.T_total ? p.T_total : b);
+    } else {
+      a = (int64_t)nn * p.T;
+      b = a + p.T;
     }
-    lds_barrier();
-    const int sub = lane & 7;
-    for (int base = 0; base < p.N; base += F::NTHR / 8) {
-      const int i = base + (tid >> 3);
-      const int li = i < p.N ? lens[i] : 0;
-      int r = 0;
-      for (int j = sub; j < p.N; j += 8) {
-        const int lj = lens[j];
-        r += (lj > li || (lj == li && j < i)) ? 1 : 0;
-      }
-      const float rank = group_sum<8>((float)r);  // exact: at most kMaxAutoOrderSeqs
-      if (i < p.N && sub == 0 && (int)rank == n) sm.pick = i;
+  };
+  int vt_idx = 0, h = 0, n = 0;
+  int64_t s0 = 0, s1 = 0;
+  int64_t rec0 = 0;  // split: the workspace slot of the work item's first chunk
+  if constexpr (MODE == kModePrep) {
+    // Block j * H + h prepares the chunk in slot j of head h.  Slots of sequence nn
+    // start at floor(start(nn) / chunk_rows) + nn, which grows strictly with nn: a
+    // bounded binary search finds the sequence; slots between sequences exit.
+    h = (int)(blockIdx.x % (unsigned)p.H);
+    const int64_t j = blockIdx.x / (unsigned)p.H;
+    const int64_t CRl = p.chunk_rows;
+    auto first_slot = [&](int nn) -> int64_t {
+      int64_t a, b;
+      seq_bounds(nn, a, b);
+      return a / CRl + nn;
+    };
+    int lo = 0, hi = p.N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (first_slot(mid) <= j) lo = mid;
+      else hi = mid - 1;
     }
-    lds_barrier();
-    n = sm.pick;
-  }
-  int64_t s0, s1;
-  if (p.cu != nullptr) {
-    s0 = p.cu[n];
-    s1 = p.cu[n + 1];
-    s0 = s0 < 0 ? 0 : (s0 > p.T_total ? p.T_total : s0);
-    s1 = s1 < s0 ? s0 : (s1 > p.T_total ? p.T_total : s1);
+    n = lo;
+    int64_t a, b;
+    seq_bounds(n, a, b);
+    const int64_t c = j - (a / CRl + n);
+    if (c < 0 || c * CRl >= b - a) return;  // uniform per workgroup
+    s0 = a + c * CRl;
+    s1 = s0 + CRl < b ? s0 + CRl : b;
+    rec0 = j;
   } else {
-    s0 = (int64_t)n * p.T;
-    s1 = s0 + p.T;
+    const int grp = 8 * p.n_vtiles;
+    vt_idx = (int)(blockIdx.x % grp) / 8;
+    const int unit = (int)(blockIdx.x / grp) * 8 + (int)(blockIdx.x % 8);
+    if (unit >= p.N * p.H) return;  // uniform per workgroup
+    h = unit % p.H;
+    // Workgroups are dispatched in index order, so a caller's sequence order (for
+    // example longest first) decides which sequences start first; it never changes
+    // what a workgroup computes.  Entries are clamped into [0, N).
+    n = unit / p.H;
+    if (p.order != nullptr) {
+      const int o = p.order[n];
+      n = o < 0 ? 0 : (o >= p.N ? p.N - 1 : o);
+    } else if (p.auto_order) {  // uniform
+      // Longest first without a caller order (packed batches of at most
+      // kMaxAutoOrderSeqs sequences whose workgroups outnumber the CUs): every
+      // workgroup ranks the lengths, ties by index, and takes the sequence whose rank
+      // is its slot.  Eight lanes share a candidate and sum its rank over their
+      // share of the others; the prefix tile, not in use yet, holds the lengths.
+      int* lens = reinterpret_cast<int*>(&sm.G[0][0]);
+      for (int i = tid; i < p.N; i += F::NTHR) {
+        const int64_t l = p.cu[i + 1] - p.cu[i];
+        lens[i] = l < 0 ? 0 : (l > 0x7fffffff ? 0x7fffffff : (int)l);
+      }
+      lds_barrier();
+      const int sub = lane & 7;
+      for (int base = 0; base < p.N; base += F::NTHR / 8) {
+        const int i = base + (tid >> 3);
+        const int li = i < p.N ? lens[i] : 0;
+        int r = 0;
+        for (int j = sub; j < p.N; j += 8) {
+          const int lj = lens[j];
+          r += (lj > li || (lj == li && j < i)) ? 1 : 0;
+        }
+        const float rank = group_sum<8>((float)r);  // exact: at most kMaxAutoOrderSeqs
+        if (i < p.N && sub == 0 && (int)rank == n) sm.pick = i;
+      }
+      lds_barrier();
+      n = sm.pick;
+    }
+    seq_bounds(n, s0, s1);
+    if constexpr (MODE == kModeRecur) rec0 = s0 / p.chunk_rows + n;
   }
   const int64_t H = p.H;
   // Chunks of CR tokens; CR < C leaves the tile's last rows empty, which the ragged
@@ -597,7 +649,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
 
   // The block above the diagonal of Mqk is never written: zero it once.
   if constexpr (F::CT == 2) {
-    for (int i = tid; i < 2 * 16 * 16; i += F::NTHR) {
+    constexpr int kSlots = MODE == kModePrep ? 1 : 2;
+    for (int i = tid; i < kSlots * 16 * 16; i += F::NTHR) {
       const int b = i >> 8, r = (i >> 4) & 15, c = 16 + (i & 15);
       sm.slot[b].Mqk[r][c] = 0;
     }
@@ -999,13 +1052,141 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     }
   };
 
+  // ======================= split: prepared-chunk records ======================
+  // A record is the byte image of what the state side reads from LDS for one
+  // chunk: Qc, Kc (shared tiles), then Kr, SOL, Mqk and a of its slot, in 16-byte
+  // units.  The prep kernel stores it, the recurrent kernel's job waves load it one
+  // chunk ahead (as q and k are loaded in the fused kernel) and copy it into LDS.
+  constexpr int kQU = F::C * F::LDQ * 2 / 16;
+  constexpr int kRU = F::C * F::LDR * 2 / 16;
+  constexpr int kCU = F::C * F::LDC * 2 / 16;
+  constexpr int kAU = F::D * 4 / 16;
+  constexpr int kRecUnits = 2 * kQU + kRU + 2 * kCU + kAU;
+  static_assert(kRecUnits * 16 == kda_record_bytes(D, C), "record layout");
+  constexpr int kRecPerJob = (kRecUnits + F::NJW * 64 - 1) / (F::NJW * 64);
+  auto rec_lds = [&](Slot<F>& sl, int u) -> u32x4_t* {
+    char* b;
+    int o;
+    if (u < kQU) { b = reinterpret_cast<char*>(&sm.Qc[0][0]); o = u; }
+    else if (u < 2 * kQU) { b = reinterpret_cast<char*>(&sm.Kc[0][0]); o = u - kQU; }
+    else if (u < 2 * kQU + kRU) { b = reinterpret_cast<char*>(&sl.Kr[0][0]); o = u - 2 * kQU; }
+    else if (u < 2 * kQU + kRU + kCU) {
+      b = reinterpret_cast<char*>(&sl.SOL[0][0]);
+      o = u - 2 * kQU - kRU;
+    } else if (u < 2 * kQU + kRU + 2 * kCU) {
+      b = reinterpret_cast<char*>(&sl.Mqk[0][0]);
+      o = u - 2 * kQU - kRU - kCU;
+    } else {
+      b = reinterpret_cast<char*>(&sl.a[0]);
+      o = u - 2 * kQU - kRU - 2 * kCU;
+    }
+    return reinterpret_cast<u32x4_t*>(b + 16 * o);
+  };
+  // The head's workspace through a descriptor of its extent: an access past it
+  // (only a malformed cu_seqlens can ask for one) reads zero or is dropped.
+  auto ws_rsrc = [&]() {
+    return make_rsrc(static_cast<char*>(p.ws) + (int64_t)h * p.ws_head_bytes,
+                     (int)p.ws_head_bytes);
+  };
+  u32x4_t rec_raw[kRecPerJob];
+  auto load_rec = [&](int c) {
+    const __amdgpu_buffer_rsrc_t rw = ws_rsrc();
+    const uint32_t base = (uint32_t)((rec0 + c) * (int64_t)(kRecUnits * 16));
+#pragma unroll
+    for (int i = 0; i < kRecPerJob; ++i) {
+      const int u = jtid + F::NJW * 64 * i;
+      if (u < kRecUnits)
+        rec_raw[i] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, base + 16u * u, 0, 0));
+    }
+  };
+  auto store_rec = [&](Slot<F>& sl) {
+#pragma unroll
+    for (int i = 0; i < kRecPerJob; ++i) {
+      const int u = jtid + F::NJW * 64 * i;
+      if (u < kRecUnits) *rec_lds(sl, u) = rec_raw[i];
+    }
+  };
+  auto record_out = [&](Slot<F>& sl) {
+    const __amdgpu_buffer_rsrc_t rw = ws_rsrc();
+    const uint32_t base = (uint32_t)(rec0 * (int64_t)(kRecUnits * 16));
+    for (int u = tid; u < kRecUnits; u += F::NTHR)
+      __builtin_amdgcn_raw_buffer_store_b128(*rec_lds(sl, u), rw, base + 16u * u, 0, 0);
+  };
+  // beta alone (the prep kernel does not stage values)
+  auto load_b = [&](const Chunk& ck) {
+    raw_b = __builtin_amdgcn_raw_buffer_load_b16(
+        make_rsrc(p.beta + ck.tok * H + ck.h, ck.valid * (int)H * 2), off_b, 0, 0);
+  };
+  auto stage_b = [&](Slot<F>& nxt, int nxt_valid) {
+    if (jtid < C) nxt.beta[jtid] = jtid < nxt_valid ? fast_sigmoid(bf2f((u16)raw_b)) : 0.f;
+  };
+
   // ======================= schedule ==========================================
   // Step s: the state side of chunk s (A: P, O0, decay, R; B: solve, update,
   // output), the chunk-local matrices of chunk s (A) and the preparation of
   // chunk s+1 (A: gate, prefix, value tile; B: norms and operands); two
   // LDS-only barriers per step, the same count on every wave.
   const int c1st = nchunks > 1 ? 1 : 0;
-  if constexpr (F::SPLIT) {
+  if constexpr (MODE == kModePrep) {
+    // one chunk: gate (state waves) and beta (job waves), the operands (every
+    // wave), the chunk-local matrices (job waves), then the record
+    if (is_state) load_g(ck(0));
+    else load_b(ck(0));
+    load_qk(ck(0));
+    if (is_state) gate(sm.slot[0], chunk_valid(0));
+    else stage_b(sm.slot[0], chunk_valid(0));
+    lds_barrier();
+    prep_B(sm.slot[0]);
+    lds_barrier();
+    if (!is_state) chunk_matrices(sm.slot[0]);
+    lds_barrier();
+    record_out(sm.slot[0]);
+  } else if constexpr (MODE == kModeRecur) {
+    // the fused schedule's state side; the job waves stage the value tile and copy
+    // the records in where the fused kernel prepares the chunk
+    if (is_state) {
+      state_in(sbase0);
+      state_cvt();
+      if (nchunks > 0) {
+        lds_barrier();
+        lds_barrier();
+        for (int s = 0; s < nchunks; ++s) {
+          Slot<F>& cur = sm.slot[s & 1];
+          state_A(cur);
+          state_R(cur);
+          lds_barrier();
+          state_B(cur, ck(s));
+          lds_barrier();
+        }
+      }
+      state_out(sbase0);
+    } else if (nchunks > 0) {
+      load_vb(ck(0));
+      load_rec(0);
+      stage_vb(sm.slot[0], chunk_valid(0));
+      load_vb(ck(c1st));
+      lds_barrier();
+      store_rec(sm.slot[0]);
+      load_rec(c1st);
+      lds_barrier();
+      for (int s = 0; s < nchunks; ++s) {
+        Slot<F>& nxt = sm.slot[(s + 1) & 1];
+        const bool more = s + 1 < nchunks;  // uniform
+        const int nxt2 = s + 2 < nchunks ? s + 2 : nchunks - 1;
+        if (more) {
+          stage_vb(nxt, chunk_valid(s + 1));
+          load_vb(ck(nxt2));
+        }
+        lds_barrier();
+        if (more) {
+          store_rec(nxt);
+          load_rec(nxt2);
+        }
+        lds_barrier();
+      }
+    }
+  } else if constexpr (F::SPLIT) {
     if (is_state) {
       state_in(sbase0);
       state_cvt();
@@ -1110,14 +1291,18 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   }
 }
 
-template <int D, int C, int VT, int NW, int NSW>
+template <int D, int C, int VT, int NW, int NSW, int MODE = kModeFused>
 hipError_t launch_one(const KdaParams& p, hipStream_t stream) {
-  // one block per unit with one value tile; otherwise whole groups of eight units
+  // one block per unit with one value tile; otherwise whole groups of eight units;
+  // the prep kernel: one block per workspace slot and head
   const int64_t units = (int64_t)p.N * p.H;
-  const int64_t blocks = p.n_vtiles == 1 ? units : (units + 7) / 8 * 8 * p.n_vtiles;
+  const int64_t blocks =
+      MODE == kModePrep ? kda_split_slots(p.T_total, p.N, p.chunk_rows) * p.H
+      : p.n_vtiles == 1 ? units
+                        : (units + 7) / 8 * 8 * p.n_vtiles;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((kda_fwd_kernel<D, C, VT, NW, NSW>), dim3((unsigned)blocks), dim3(NW * 64), 0,
-                     stream, p);
+  hipLaunchKernelGGL((kda_fwd_kernel<D, C, VT, NW, NSW, MODE>), dim3((unsigned)blocks),
+                     dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1191,6 +1376,33 @@ bool kda_schedule_supported(int D, int chunk, int v_tile) {
   KDA_SCHEDULES(KDA_SUPPORTED)
 #undef KDA_SUPPORTED
   return false;
+}
+
+// The split's schedules: (D, chunk, value tile, waves, state waves) of the
+// recurrent kernel; the prep kernel of a chunk length is the first of its row.
+#define KDA_SPLIT_SCHEDULES(X) \
+  X(128, 32, 128, 8, 4)        \
+  X(128, 32, 64, 8, 4)         \
+  X(128, 16, 128, 8, 4)
+
+bool kda_split_supported(int D, int chunk, int v_tile) {
+#define KDA_SPLIT_SUPPORTED(d, c, vt, nw, nsw) \
+  if (D == d && chunk == c && v_tile == vt) return true;
+  KDA_SPLIT_SCHEDULES(KDA_SPLIT_SUPPORTED)
+#undef KDA_SPLIT_SUPPORTED
+  return false;
+}
+
+hipError_t launch_kda_split(const KdaParams& p, int D, int chunk, int v_tile, hipStream_t stream) {
+  if (!kda_split_supported(D, chunk, v_tile)) return hipErrorInvalidValue;
+  hipError_t e = chunk == 32 ? launch_one<128, 32, 128, 8, 4, kModePrep>(p, stream)
+                             : launch_one<128, 16, 128, 8, 4, kModePrep>(p, stream);
+  if (e != hipSuccess) return e;
+#define KDA_SPLIT_LAUNCH(d, c, vt, nw, nsw) \
+  if (D == d && chunk == c && v_tile == vt) return launch_one<d, c, vt, nw, nsw, kModeRecur>(p, stream);
+  KDA_SPLIT_SCHEDULES(KDA_SPLIT_LAUNCH)
+#undef KDA_SPLIT_LAUNCH
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_kda_fwd(const KdaParams& p, int D, int chunk, int v_tile, hipStream_t stream) {

@@ -36,13 +36,40 @@ struct KdaParams {
   float lam2_floor;         // smallest per-token base-2 decay kept (-236 in one-token chunks
                             // when lb2 < -236, else -infinity: no floor)
   float anchor;             // fixed base-2 exponent anchor of the chunk
+  // Two-kernel split only: the prepared-chunk workspace.  Head h owns ws_head_bytes
+  // bytes at ws + h * ws_head_bytes, one record of kda_record_bytes(D, C) bytes per
+  // slot; chunk c of sequence n sits in slot floor(start(n) / chunk_rows) + n + c.
+  void* ws;
+  int64_t ws_head_bytes;
 };
+
+// Bytes of one prepared-chunk record for head dimension D and tile height C: the
+// byte images of the centred operands Qc and Kc ([C][D+8] bf16 each), the decayed
+// keys Kr ([C][D+16] bf16), the solve operands and Mqk ([C][C+8] bf16 each) and the
+// chunk decay a (D fp32), as the recurrent side reads them from LDS.
+constexpr int64_t kda_record_bytes(int64_t D, int64_t C) {
+  return 2 * C * (D + 8) * 2 + C * (D + 16) * 2 + 2 * C * (C + 8) * 2 + D * 4;
+}
+
+// Slots per head of a split workspace: chunk starts never share a slot, and none
+// exceeds floor(T_total / chunk_rows) + num_seqs.
+constexpr int64_t kda_split_slots(int64_t T_total, int64_t num_seqs, int64_t chunk_rows) {
+  return T_total / chunk_rows + num_seqs + 1;
+}
 
 // Launches the fused forward for a resolved schedule; returns a hipError_t.
 hipError_t launch_kda_fwd(const KdaParams& p, int D, int chunk, int v_tile, hipStream_t stream);
 
 // Whether a (D, chunk, v_tile) schedule has a compiled kernel.
 bool kda_schedule_supported(int D, int chunk, int v_tile);
+
+// The two-kernel split: a token-parallel kernel writes every chunk's record into
+// p.ws, then the recurrent kernel reads them back (same schedule as the fused
+// kernel).  Both are enqueued on `stream`; returns a hipError_t.
+hipError_t launch_kda_split(const KdaParams& p, int D, int chunk, int v_tile, hipStream_t stream);
+
+// Whether the split has compiled kernels for a (D, chunk, v_tile) schedule.
+bool kda_split_supported(int D, int chunk, int v_tile);
 
 // Largest num_seqs the on-device longest-first ordering handles (one workgroup
 // sorts all lengths in LDS).

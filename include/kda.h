@@ -63,6 +63,7 @@ extern "C" {
 #define KDA_ERR_BAD_SCALE (-7)       /* scale not finite                                 */
 #define KDA_ERR_BAD_SCHEDULE (-8)    /* unsupported forced chunk size or value tile      */
 #define KDA_ERR_HIP (-9)             /* the HIP runtime reported an error at launch      */
+#define KDA_ERR_BAD_WORKSPACE (-10)  /* kda_fwd_split: workspace smaller than required   */
 
 /* State dtype codes (initial_state_dtype, final_state_dtype). */
 #define KDA_DTYPE_BF16 0
@@ -181,6 +182,48 @@ int kda_fwd_transposed_state(const void* q, const void* k, const void* v, const 
                              int initial_state_dtype, void* final_state, int final_state_dtype,
                              const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T,
                              int64_t H, int64_t D, void* stream);
+
+/*
+ * kda_split_workspace_bytes -- bytes of the workspace kda_fwd_split needs.
+ *   T_total     tokens of the flattened batch (B * T).
+ *   num_seqs    N, as for kda_fwd.
+ *   H, D        heads and head dimension; the split runs D = 128 only.
+ *   lower_bound, chunk_size  as for kda_fwd_sched (0: automatic chunk length).
+ * One record per slot and head: the prepared operands of one chunk (Qc, Kc, Kr,
+ * the solve operands, Mqk and the decay, in the layout the recurrent kernel copies
+ * into LDS; 32,256 bytes at 32-token chunks).  A head has floor(T_total / chunk)
+ * + num_seqs + 1 slots.  Returns the size, or a negative status
+ * (KDA_ERR_BAD_SHAPE, KDA_ERR_BAD_LOWER_BOUND, KDA_ERR_BAD_SCHEDULE).
+ */
+int64_t kda_split_workspace_bytes(int64_t T_total, int64_t num_seqs, int64_t H, int64_t D,
+                                  float lower_bound, int chunk_size);
+
+/*
+ * kda_fwd_split -- kda_fwd as two kernels, the organisation of FlashKDA's
+ * prep and recurrent kernels that the FlashInfer PR #4262 summary describes
+ * (its workspace of chunk-local matrices and transformed Q and K between them).
+ * A token-parallel kernel prepares every chunk of every head (gate, prefix,
+ * norms, centred operands, Mqk and the inverted diagonal blocks) and writes it to
+ * `workspace`.  The recurrent kernel then reads those records back in chunk order
+ * and runs only the state side, on value tiles of v_tile rows.
+ *   workspace        caller-owned device memory of at least
+ *                    kda_split_workspace_bytes(B * T, num_seqs, H, D, lower_bound, 0)
+ *                    bytes (KDA_ERR_BAD_WORKSPACE otherwise, KDA_ERR_NULL_ARG when NULL).
+ *                    It must not overlap any other argument (KDA_ERR_BAD_ALIAS).  Its
+ *                    contents on entry do not matter and are scratch on return.
+ *   workspace_bytes  its size in bytes.
+ *   v_tile           0 (automatic, as for kda_fwd), 128, or 64 at 32-token chunks;
+ *                    other schedules are KDA_ERR_BAD_SCHEDULE, as is D != 128.
+ * The results are bitwise those of kda_fwd_sched with the same value tile: both
+ * kernels run the fused kernel's own preparation and state-side code.  Both are
+ * enqueued on `stream`.  Everything else is exactly as kda_fwd.
+ */
+int kda_fwd_split(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                  float scale, void* out, const float* A_log, const float* dt_bias,
+                  float lower_bound, const void* initial_state, int initial_state_dtype,
+                  void* final_state, int final_state_dtype, const int64_t* cu_seqlens,
+                  int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t D, void* stream,
+                  void* workspace, int64_t workspace_bytes, int v_tile);
 
 /*
  * kda_longest_first -- writes the longest-first order of a packed batch for

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, -10, -1):
+    for code in range(0, -11, -1):
         s = kda.kda_status_string(code)
         assert s.startswith("KDA_")
     assert "UNKNOWN" in kda.kda_status_string(-1234)
@@ -215,3 +215,51 @@ def test_ordered_and_longest_first_validation(lib):
     assert lf(11 * GB, 0, 12 * GB, None) == kda.KDA_ERR_BAD_VARLEN
     assert lf(11 * GB, 8193, 12 * GB, None) == kda.KDA_ERR_BAD_VARLEN
     assert lf(11 * GB, 4, 11 * GB + 8, None) == kda.KDA_ERR_BAD_ALIAS
+
+
+def test_split_workspace_bytes(lib):
+    """One record per slot and head: the byte images of Qc, Kc ([C][D+8] bf16), Kr
+    ([C][D+16] bf16), the solve operands and Mqk ([C][C+8] bf16) and the decay (D fp32);
+    floor(T_total / chunk) + num_seqs + 1 slots per head."""
+    rec32 = 2 * 32 * 136 * 2 + 32 * 144 * 2 + 2 * 32 * 40 * 2 + 128 * 4
+    rec16 = 2 * 16 * 136 * 2 + 16 * 144 * 2 + 2 * 16 * 24 * 2 + 128 * 4
+    assert rec32 == 32256 and rec16 == 15360
+    ws = kda.kda_split_workspace_bytes
+    assert ws(32768, 1, 96, 128, -5.0) == 96 * (1024 + 2) * rec32
+    assert ws(2024, 3, 96, 128, -5.0) == 96 * (63 + 4) * rec32
+    assert ws(2024, 3, 96, 128, -8.0) == 96 * (126 + 4) * rec16       # automatic: 16 tokens
+    assert ws(2024, 3, 96, 128, -5.0, 8) == 96 * (253 + 4) * rec16    # 8 tokens in 16 rows
+    assert ws(0, 5, 2, 128, -1.0) == 2 * 6 * rec32                   # every sequence empty
+    raw = lib.kda_split_workspace_bytes
+    assert raw(2024, 3, 96, 64, -5.0, 0) == kda.KDA_ERR_BAD_SCHEDULE  # D = 128 only
+    assert raw(2024, 3, 96, 128, 0.0, 0) == kda.KDA_ERR_BAD_LOWER_BOUND
+    assert raw(2024, 3, 96, 128, -6.0, 32) == kda.KDA_ERR_BAD_LOWER_BOUND
+    assert raw(2024, 3, 96, 128, -5.0, 24) == kda.KDA_ERR_BAD_SCHEDULE
+    assert raw(2024, 0, 96, 128, -5.0, 0) == kda.KDA_ERR_BAD_SHAPE
+    assert raw(2024, 3, 0, 128, -5.0, 0) == kda.KDA_ERR_BAD_SHAPE
+    # a head's records must stay below 2^31 bytes (31-bit offsets)
+    assert raw(1 << 22, 1, 1, 128, -5.0, 0) == kda.KDA_ERR_BAD_SHAPE
+    assert raw(1 << 20, 1, 1, 128, -5.0, 0) == ((1 << 15) + 2) * rec32
+
+
+def _split(ws, ws_bytes, vt=0, **kw):
+    a = _args(**kw)
+    return kda.load_library().kda_fwd_split(*a[:-2], None, ws, ws_bytes, vt)
+
+
+def test_split_validation(lib):
+    """Error paths of kda_fwd_split return before any launch."""
+    need = kda.kda_split_workspace_bytes(2 * 64, 2, 4, 128, -5.0)
+    assert _split(None, need) == kda.KDA_ERR_NULL_ARG
+    assert _split(12 * GB, need - 1) == kda.KDA_ERR_BAD_WORKSPACE
+    assert _split(12 * GB, need, D=64) == kda.KDA_ERR_BAD_SCHEDULE
+    assert _split(12 * GB, need, vt=32) == kda.KDA_ERR_BAD_SCHEDULE
+    # 16-token chunks run the split at value tile 128 only
+    assert _split(12 * GB, 1 << 40, vt=64, lb=-8.0) == kda.KDA_ERR_BAD_SCHEDULE
+    # the workspace is written: it may overlap no other buffer
+    assert _split(1 * GB, need) == kda.KDA_ERR_BAD_ALIAS
+    assert _split(9 * GB + 64, need) == kda.KDA_ERR_BAD_ALIAS
+    assert _split(11 * GB - 16, need, B=1, T=128, N=2, has_cu=True) == kda.KDA_ERR_BAD_ALIAS
+    # everything kda_fwd rejects is still rejected
+    assert _split(12 * GB, need, lb=1.0) == kda.KDA_ERR_BAD_LOWER_BOUND
+    assert _split(12 * GB, need, q=None) == kda.KDA_ERR_NULL_ARG

@@ -1,0 +1,133 @@
+"""GPU tests of the two-kernel split (`kda_fwd_split`).
+
+The split runs the fused kernel's own preparation code in a token-parallel kernel, which
+writes every chunk's operands to the workspace, and its own state-side code in the
+recurrent kernel, which reads them back.  So its results must equal `kda_fwd_sched` at the
+same value tile bit for bit, on every workload shape: batched and packed sequences, empty
+and one-token sequences, short chunks, both state dtypes, NULL states, the in-place alias and
+the kernel's own longest-first order.  One case also checks the split against the fp64
+oracle directly (max-abs 2e-2, rel-L2 5e-3, the tolerance of the other parity tests).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_62_amd as kda
+import oracle
+from gated_delta_rule_62_amd.workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _workspace(inp, w, fill=0xFF):
+    T_total = inp["q"].shape[0] * inp["q"].shape[1]
+    N = inp["cu_seqlens"].numel() - 1 if inp["cu_seqlens"] is not None else inp["q"].shape[0]
+    n = kda.kda_split_workspace_bytes(T_total, N, w.H, w.D, w.lower_bound, w.chunk_size)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws.fill_(fill)  # every record the recurrent kernel reads is written first
+    return ws
+
+
+def _run_both(w, vt=0, inplace=False):
+    # the split takes the automatic chunk length; so does the fused run it is compared with
+    assert w.chunk_size == 0
+    print("case: %s B=%d T=%d H=%d lengths=%s lb=%g state %s->%s vt=%d inplace=%s"
+          % (w.name, w.B, w.T, w.H, w.lengths, w.lower_bound, w.state_in, w.state_out, vt,
+             inplace), flush=True)
+    inp = make_inputs(w, device="cuda")
+    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"])
+    tail = (inp["A_log"], inp["dt_bias"], inp["lower_bound"])
+    ws = _workspace(inp, w)
+    out_f = torch.full_like(inp["out"], float("nan"))
+    out_s = torch.full_like(inp["out"], float("nan"))
+    s0 = inp["initial_state"]
+    if inplace:
+        st_f, st_s = s0.clone(), s0.clone()
+        kda.kda_fwd_sched(*args, out_f, *tail, st_f, st_f, inp["cu_seqlens"], 0, vt)
+        kda.kda_fwd_split(*args, out_s, *tail, ws, st_s, st_s, inp["cu_seqlens"], vt)
+        fin_f, fin_s = st_f, st_s
+    else:
+        fin_f = None if inp["final_state"] is None else torch.full_like(inp["final_state"], 7.0)
+        fin_s = None if fin_f is None else torch.full_like(fin_f, 7.0)
+        kda.kda_fwd_sched(*args, out_f, *tail, s0, fin_f, inp["cu_seqlens"], 0, vt)
+        kda.kda_fwd_split(*args, out_s, *tail, ws, s0, fin_s, inp["cu_seqlens"], vt)
+    torch.cuda.synchronize()
+    return inp, out_f, out_s, fin_f, fin_s
+
+
+def _bitwise(a, b, what):
+    assert not torch.isnan(a.float()).any(), what + ": unwritten elements"
+    assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                       b.view(torch.int16) if b.dtype == torch.bfloat16 else b), what
+
+
+@pytest.mark.parametrize("name,vt", [("batched", 128), ("batched", 64), ("varlen3", 0),
+                                     ("many", 0), ("small", 0)])
+def test_split_equals_fused_on_the_workloads(name, vt):
+    w = WORKLOADS[name]
+    if w.D != 128 or w.chunk_size != 0:  # the small workload: D = 32, forced 16-token chunks
+        w = Workload(w.name + "_d128", B=w.B, T=w.T, H=w.H, D=128, seed=w.seed,
+                     lengths=w.lengths, state_in=w.state_in, state_out=w.state_out,
+                     lower_bound=w.lower_bound)
+    _, out_f, out_s, fin_f, fin_s = _run_both(w, vt)
+    _bitwise(out_s, out_f, "out")
+    if fin_f is not None:
+        _bitwise(fin_s, fin_f, "final_state")
+
+
+def test_split_equals_fused_long_two_value_tiles():
+    """The long workload (one 32768-token sequence, 96 heads): the automatic value tile is
+    64, two workgroups per head, which the split serves without repeating the preparation."""
+    _, out_f, out_s, fin_f, fin_s = _run_both(WORKLOADS["long"], 64)
+    _bitwise(out_s, out_f, "out")
+    _bitwise(fin_s, fin_f, "final_state")
+
+
+@pytest.mark.parametrize("lb,state", [(-5.0, "fp32"), (-8.0, "bf16"), (-40.0, None),
+                                      (-300.0, "zero_bf16")])
+def test_split_edge_lengths_and_short_chunks(lb, state):
+    """Empty, one-token and ragged sequences; 16-token chunks (lb = -8), 4-token chunks in
+    the 16-row tile (lb = -40) and one-token chunks with the decay floor (lb = -300)."""
+    w = Workload("split_edges", B=1, T=0, H=3, D=128, seed=71, lengths=[0, 1, 3, 33, 0, 70, 17],
+                 state_in=state, state_out="fp32" if state == "fp32" else "bf16",
+                 lower_bound=lb)
+    _, out_f, out_s, fin_f, fin_s = _run_both(w)
+    _bitwise(out_s, out_f, "out")
+    _bitwise(fin_s, fin_f, "final_state")
+
+
+def test_split_in_place_state_and_ragged_batch():
+    w = Workload("split_inplace", B=3, T=77, H=4, D=128, seed=72, state_in="bf16",
+                 state_out="bf16")
+    _, out_f, out_s, fin_f, fin_s = _run_both(w, inplace=True)
+    _bitwise(out_s, out_f, "out")
+    _bitwise(fin_s, fin_f, "final_state")
+
+
+def test_split_matches_the_oracle():
+    w = Workload("split_oracle", B=1, T=0, H=4, D=128, seed=73, lengths=[150, 0, 1, 90],
+                 state_in="fp32", state_out="fp32", lower_bound=-3.0)
+    inp, _, out_s, _, fin_s = _run_both(w)
+    out_ref, fin_ref = oracle.kda_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                      inp["scale"], inp["A_log"], inp["dt_bias"],
+                                      inp["lower_bound"], inp["initial_state"],
+                                      inp["cu_seqlens"])
+    for x, ref, what in ((out_s, out_ref, "out"), (fin_s, fin_ref, "final_state")):
+        x = x.to("cpu", torch.float64).numpy()
+        mx = float(np.abs(x - ref).max())
+        rel = float(np.linalg.norm(x - ref) / np.linalg.norm(ref))
+        print("%s: max-abs %.3e rel-L2 %.3e" % (what, mx, rel), flush=True)
+        assert mx <= 2e-2 and rel <= 5e-3, (what, mx, rel)
+
+
+def test_split_errors_raise_before_launch():
+    w = Workload("split_err", B=1, T=64, H=2, D=128, seed=74, state_in="bf16")
+    inp = make_inputs(w, device="cuda")
+    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["scale"], inp["out"],
+            inp["A_log"], inp["dt_bias"], inp["lower_bound"])
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(kda.KdaError) as e:
+        kda.kda_fwd_split(*args, small, inp["initial_state"], inp["final_state"])
+    assert e.value.status == kda.KDA_ERR_BAD_WORKSPACE
