@@ -84,7 +84,11 @@ int resolve(const void* q, const void* k, const void* v, const void* g, const vo
             const void* final_state, int final_state_dtype, const int64_t* cu_seqlens,
             int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t D, int chunk_size,
             int v_tile, const int32_t* seq_order, int* chunk_out, int* v_tile_out) {
-  if (!q || !k || !v || !g || !beta || !out || !A_log || !dt_bias) return KDA_ERR_NULL_ARG;
+  // With no tokens (every sequence empty) the kernels touch no activation buffer, so
+  // those pointers may be NULL, as a zero-element tensor's are.
+  const bool tokens = B > 0 && T > 0;
+  if ((tokens && (!q || !k || !v || !g || !beta || !out)) || !A_log || !dt_bias)
+    return KDA_ERR_NULL_ARG;
   if (B < 1 || H < 1 || T < 0) return KDA_ERR_BAD_SHAPE;
   if (T == 0 && cu_seqlens == nullptr) return KDA_ERR_BAD_SHAPE;
   if (D != 32 && D != 64 && D != 128) return KDA_ERR_BAD_SHAPE;

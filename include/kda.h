@@ -47,7 +47,8 @@ extern "C" {
 
 /* Status codes. */
 #define KDA_OK 0
-#define KDA_ERR_NULL_ARG (-1)        /* a required pointer is NULL                      */
+#define KDA_ERR_NULL_ARG (-1)        /* a required pointer is NULL (q, k, v, g, beta and */
+                                     /* out may be NULL when B * T == 0)                */
 #define KDA_ERR_BAD_SHAPE (-2)       /* B,T,H < 1 (T may be 0 only with cu_seqlens),     */
                                      /* D not in {32, 64, 128}, H * D >= 2^25,            */
                                      /* B * T > 2^40, num_seqs * H > 2^29, or an          */

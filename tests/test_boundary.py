@@ -101,6 +101,10 @@ def test_valid_calls(lib):
 def test_null_and_shape_errors(lib):
     for name in ("q", "k", "v", "g", "beta", "out", "A_log", "dt_bias"):
         assert _check(**{name: None}) == kda.KDA_ERR_NULL_ARG, name
+    # with every sequence empty no activation buffer is touched: NULL is accepted for them
+    empty = dict(B=1, T=0, N=3, has_cu=True)
+    assert _check(q=None, k=None, v=None, g=None, beta=None, out=None, **empty) == kda.KDA_OK
+    assert _check(A_log=None, **empty) == kda.KDA_ERR_NULL_ARG
     assert _check(B=0) == kda.KDA_ERR_BAD_SHAPE
     assert _check(H=0) == kda.KDA_ERR_BAD_SHAPE
     assert _check(T=0) == kda.KDA_ERR_BAD_SHAPE

@@ -98,6 +98,18 @@ def test_split_edge_lengths_and_short_chunks(lb, state):
     _bitwise(fin_s, fin_f, "final_state")
 
 
+def test_every_sequence_empty_passes_states_through():
+    """A packed batch of empty sequences: the activation tensors have no elements (NULL
+    pointers) and both entry points copy each initial state to the final state."""
+    w = Workload("all_empty", B=1, T=0, H=3, D=128, seed=75, lengths=[0, 0, 0],
+                 state_in="fp32", state_out="bf16")
+    _, out_f, out_s, fin_f, fin_s = _run_both(w)
+    assert out_s.numel() == 0
+    _bitwise(fin_s, fin_f, "final_state")
+    inp = make_inputs(w, device="cuda")
+    assert torch.equal(fin_f, inp["initial_state"].to(torch.bfloat16))
+
+
 def test_split_in_place_state_and_ragged_batch():
     w = Workload("split_inplace", B=3, T=77, H=4, D=128, seed=72, state_in="bf16",
                  state_out="bf16")
