@@ -4,6 +4,7 @@ kda_fwd_check only compares pointer values and sizes)."""
 from __future__ import annotations
 
 import math
+import random
 import os
 import re
 
@@ -267,3 +268,32 @@ def test_split_validation(lib):
     # everything kda_fwd rejects is still rejected
     assert _split(12 * GB, need, lb=1.0) == kda.KDA_ERR_BAD_LOWER_BOUND
     assert _split(12 * GB, need, q=None) == kda.KDA_ERR_NULL_ARG
+
+
+def test_split_slot_numbering_is_injective_and_fits():
+    """The split files chunk c of sequence n under slot floor(start(n) / chunk) + n + c.
+    The prep kernel finds a slot's sequence by binary search over first slots, and the
+    workspace holds floor(T_total / chunk) + num_seqs + 1 slots per head.  Over random
+    packed batches (empty sequences included) and every chunk length:
+    * no two chunks share a slot;
+    * first slots grow strictly with n;
+    * every slot is below the sized count."""
+    rng = random.Random(7)
+    for _ in range(300):
+        lens = [rng.choice([0, 0, 1, rng.randint(1, 9), rng.randint(1, 300)])
+                for _ in range(rng.randint(1, 12))]
+        cu = [0]
+        for length in lens:
+            cu.append(cu[-1] + length)
+        for chunk in (32, 16, 8, 4, 2, 1):
+            slots = cu[-1] // chunk + len(lens) + 1
+            seen = set()
+            firsts = [cu[n] // chunk + n for n in range(len(lens))]
+            assert all(a < b for a, b in zip(firsts, firsts[1:]))
+            for n, length in enumerate(lens):
+                for c in range((length + chunk - 1) // chunk):
+                    j = firsts[n] + c
+                    assert j not in seen and 0 <= j < slots
+                    seen.add(j)
+                    # the binary search's answer: the last sequence whose first slot <= j
+                    assert max(m for m in range(len(lens)) if firsts[m] <= j) == n
