@@ -173,10 +173,19 @@ struct Cfg {
   // the same barriers.  With fewer waves every wave takes a share of everything
   // in one loop.
   static constexpr bool SPLIT = NW - NSW >= 4;
+  // With at least eight job waves the state waves run the recurrence only: the gate,
+  // the operands, the chunk matrices and the value tile are all the job waves' work,
+  // one chunk further ahead (the state-only schedule).  A SIMD then holds one state
+  // wave and two job waves, so the preparation's VALU work issues from two waves.
+  static constexpr bool SO = NW - NSW >= 8;
   static constexpr int JOB_BASE = SPLIT ? NSW : 0;
   static constexpr int NJW = NW - JOB_BASE;      // job waves (they also stage v and beta)
-  static constexpr int NGW = SPLIT ? NSW : NW;   // gate waves: the state waves in the split
-  static constexpr int EPT = C * D / (NW * 64);  // row layout (q, k; every wave): positions per thread
+  // gate waves: the state waves in the role split; the last four job waves in the
+  // state-only schedule (the first four take the two inversions and two other tiles)
+  static constexpr int NGW = SO ? 4 : (SPLIT ? NSW : NW);
+  static constexpr int GATE_BASE = SO ? NJW - 4 : 0;  // first gate wave among the job waves
+  static constexpr int NOW = SO ? NJW : NW;      // operand waves
+  static constexpr int EPT = C * D / (NOW * 64);  // row layout (q, k; operand waves): positions per thread
   static constexpr int TPR = D / EPT;            // threads per chunk row
   static constexpr int EPV = C * VT / (NJW * 64);  // value row layout (job waves): elements per thread
   static constexpr int TPRV = VT / EPV;          // threads per value row
@@ -187,7 +196,8 @@ struct Cfg {
   static constexpr int CPG = 64 / RG;
   static constexpr int SPASS = SCOLS / (2 * CPG);
   static constexpr int RPG = C / RG;             // chunk rows per row group
-  static constexpr int LDQ = D + 8;            // bf16 row stride of [C][D] tiles
+  static constexpr int LDQ = D + 16;           // bf16 row stride of [C][D] tiles (reads of
+                                               // 16 rows x 4 lane groups are conflict-free)
   static constexpr int LDG = D + 4;            // fp32 row stride of the prefix tile
   static constexpr int LDR = D + 16;           // bf16 row stride of the [C][D] Kr tile
   static constexpr int LDC = C + 8;            // bf16 row stride of [C][C] tiles
@@ -202,6 +212,7 @@ struct Cfg {
   static_assert(SPASS >= 1 && SPASS * 2 * CPG * NGW == D, "column layout");
   static_assert(D % 32 == 0, "head dim");
   static_assert(NJW == 2 || NJW == 4 || NJW == 8, "job assignment");
+  static_assert(!SO || NSW == 4, "state-only schedule: one state wave per SIMD");
   static_assert(C <= NJW * 64, "one beta per job thread");
 };
 
@@ -223,9 +234,20 @@ struct Chunk {
   int h;
 };
 
+// The centred operands Qc and Kc (key order).  The state-only schedule writes the
+// next chunk's while the state waves read the current chunk's, so they live in each
+// slot there; the other schedules keep one copy beside the slots.
+template <class F, bool kHere>
+struct QcKc {};
+template <class F>
+struct QcKc<F, true> {
+  u16 Qc[F::C][F::LDQ];
+  u16 Kc[F::C][F::LDQ];
+};
+
 // Prepared operands of one chunk.
 template <class F>
-struct alignas(16) Slot {
+struct alignas(16) Slot : QcKc<F, F::SO> {
   u16 Kr[F::C][F::LDR];      // columns in state-row order (read transposed)
   u16 SOL[F::C][F::LDC];     // X11 2^-16, X22 2^-16 (X = (I + L)^-1 diagonal blocks) and
                              // -L21 2^16: the solve then yields U 2^-16
@@ -236,11 +258,9 @@ struct alignas(16) Slot {
 };
 
 template <class F, int NSLOT>
-struct alignas(16) Smem {
+struct alignas(16) Smem : QcKc<F, !F::SO> {  // (Qc, Kc: the chunk whose state side,
+                             // matrices and preparation alternate in them)
   Slot<F> slot[NSLOT];       // two alternate in the chunk loop; the prep kernel uses one
-  u16 Qc[F::C][F::LDQ];      // centred operands (key order) of the chunk whose state side,
-                             // matrices and preparation alternate in them
-  u16 Kc[F::C][F::LDQ];
   u16 Ki[F::C][F::LDQ];
   float G[F::C][F::LDG];     // inclusive base-2 decay prefix of the chunk being prepared,
                              // inside its row group of the gate layout
@@ -399,6 +419,15 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   using F = Cfg<D, C, VT, NW, NSW>;
   static_assert(MODE == kModeFused || F::SPLIT, "the split runs the role-split schedules only");
   __shared__ Smem<F, MODE == kModePrep ? 1 : 2> sm;
+  // The centred operands of the chunk prepared in slot sl.
+  auto qc_of = [&](Slot<F>& sl) -> u16(*)[F::LDQ] {
+    if constexpr (F::SO) return sl.Qc;
+    else return sm.Qc;
+  };
+  auto kc_of = [&](Slot<F>& sl) -> u16(*)[F::LDQ] {
+    if constexpr (F::SO) return sl.Kc;
+    else return sm.Kc;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -510,10 +539,9 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   const float c1 = __builtin_amdgcn_exp2f(Ca + kStateExp);  // 2^(Ca + 16): restores P
   const float c1o = c1 * p.scale;                           // ... and O, with the scale
   const float c1i = __builtin_amdgcn_exp2f(-Ca);            // 2^-Ca
-  auto chunk_valid = [&](int c) -> int {
-    const int64_t rem = s1 - (s0 + (int64_t)c * CR);
-    return rem < CR ? (int)rem : CR;
-  };
+  // tokens of the last chunk (uniform; every earlier chunk holds CR)
+  const int last_valid = nchunks > 0 ? (int)(s1 - s0 - (int64_t)(nchunks - 1) * CR) : 0;
+  auto chunk_valid = [&](int c) -> int { return c >= nchunks - 1 ? last_valid : CR; };
   auto ck = [&](int c) -> Chunk { return Chunk{s0 + (int64_t)c * CR, chunk_valid(c), h}; };
   const int64_t sbase0 = ((int64_t)n * H + h) * D * D;
 
@@ -531,7 +559,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   auto kconst = [](int kt) { return 32 * (kt >> 1) + 4 * (kt & 1); };
   // state_in issues the loads of the state's raw bits into the accumulators;
   // state_cvt widens them (bf16) and applies the 2^-16 state scale.
-  auto state_in = [&](int64_t sbase) {
+  auto state_in = [&](int64_t sbase) __attribute__((always_inline)) {
 #pragma unroll
     for (int kt = 0; kt < F::KT; ++kt)
 #pragma unroll
@@ -579,7 +607,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
         S[2 * ks + 1][nt] = f32x4_t{__uint_as_float(w[2]), __uint_as_float(w[3]), 0.f, 0.f};
       }
   };
-  auto state_cvt = [&]() {
+  auto state_cvt = [&]() __attribute__((always_inline)) {
     if (p.s_in == nullptr) return;
 #pragma unroll
     for (int kt = 0; kt < F::KT; ++kt)
@@ -599,7 +627,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       }
   };
   // The state is scaled back in place and stored tile by tile.
-  auto state_out = [&](int64_t sbase) {
+  auto state_out = [&](int64_t sbase) __attribute__((always_inline)) {
     if (p.s_out == nullptr) return;
     const int es = p.s_out_fp32 ? 4 : 2;
     const __amdgpu_buffer_rsrc_t rs =
@@ -661,7 +689,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   // A: P'^T = Kc S^T and O0' = S Qc^T (P = 2^Ca P', O0 = 2^Ca O0') with the decay
   // S^T <- diag(a) S^T alongside
   // (state_A), then R^T = diag(beta)(V - P^T) in place in P (state_R).
-  auto state_A = [&](Slot<F>& cur) {
+  auto state_A = [&](Slot<F>& cur) __attribute__((always_inline)) {
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
     // one 32-row key step at a time: its bf16 copy of S^T is live only there, and
     // once it is taken the decay of those rows proceeds while the products run
@@ -680,8 +708,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       }
 #pragma unroll
       for (int ct = 0; ct < F::CT; ++ct) {
-        const u32x4_t aK = lds_op_k(&sm.Kc[16 * ct + l16][0], 32 * ks, lg);
-        const u32x4_t aQ = lds_op_k(&sm.Qc[16 * ct + l16][0], 32 * ks, lg);
+        const u32x4_t aK = lds_op_k(&kc_of(cur)[16 * ct + l16][0], 32 * ks, lg);
+        const u32x4_t aQ = lds_op_k(&qc_of(cur)[16 * ct + l16][0], 32 * ks, lg);
 #pragma unroll
         for (int nt = 0; nt < F::NTW; ++nt) {
           P[ct][nt] = mfma_k32(aK, bS[nt], ks == 0 ? zero : P[ct][nt]);
@@ -690,7 +718,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       }
     }
   };
-  auto state_R = [&](Slot<F>& cur) {
+  auto state_R = [&](Slot<F>& cur) __attribute__((always_inline)) {
 #pragma unroll
     for (int ct = 0; ct < F::CT; ++ct) {
       const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(&cur.beta[16 * ct + 4 * lg]);
@@ -711,7 +739,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   // formed; with the solve operands' power-of-two factors both halves come out
   // as U 2^-16, the state's own scale.  The output leaves as bf16 straight from
   // the accumulators, through a descriptor bounded to the chunk's valid rows.
-  auto state_B = [&](Slot<F>& cur, const Chunk& ck) {
+  auto state_B = [&](Slot<F>& cur, const Chunk& ck) __attribute__((always_inline)) {
     u32x4_t bU[F::NTW];
     {
       const u32x4_t aX11 = lds_op_pad(&cur.SOL[l16][0], lg);
@@ -733,15 +761,9 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
         for (int nt = 0; nt < F::NTW; ++nt) bU[nt] = acc_to_op_pad(Ut[nt]);
       }
     }
-    // S^T += Kr^T U^T (the decay was applied in phase A)
-#pragma unroll
-    for (int kt = 0; kt < F::KT; ++kt) {
-      const u32x4_t aR = lds_op_tr<F::LDR, F::CT == 2>(&cur.Kr[0][0], 16 * kt, l16, lg);
-#pragma unroll
-      for (int nt = 0; nt < F::NTW; ++nt) S[kt][nt] = mfma_k32(aR, bU[nt], S[kt][nt]);
-    }
     // O = 2^Ca (O0' + U Mqk'^T), Mqk' = 2^-Ca Mqk: U as the A operand (value rows),
-    // Mqk' rows as B (token columns)
+    // Mqk' rows as B (token columns).  Before the state update, so that O's
+    // accumulators are free while the update's operands are read.
     const __amdgpu_buffer_rsrc_t ro =
         make_rsrc(p.out + (ck.tok * H + ck.h) * D + vt_idx * VT, ck.valid * (int)row_bytes);
 #pragma unroll
@@ -759,20 +781,30 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
             0, 0);
       }
     }
+    // S^T += Kr^T U^T (the decay was applied in phase A)
+#pragma unroll
+    for (int kt = 0; kt < F::KT; ++kt) {
+      const u32x4_t aR = lds_op_tr<F::LDR, F::CT == 2>(&cur.Kr[0][0], 16 * kt, l16, lg);
+#pragma unroll
+      for (int nt = 0; nt < F::NTW; ++nt) S[kt][nt] = mfma_k32(aR, bU[nt], S[kt][nt]);
+    }
   };
 
   // ======================= preparation ======================================
   // Column layout (g, gate, prefix; gate waves): pass ps covers key columns
   // g_col0 + 2 CPG ps and g_col0 + 2 CPG ps + 1 (lane % CPG picks the pair) and
   // chunk rows g_row0 .. g_row0 + RPG - 1 (lane / CPG picks one of RG row groups).
-  const int gw = (F::SPLIT && !is_state) ? 0 : wave;  // index among the gate waves
+  const bool is_gate = F::SO ? (is_job && jw >= F::GATE_BASE) : (!F::SPLIT || is_state);
+  const int gw = F::SO ? (is_gate ? jw - F::GATE_BASE : 0)
+                       : ((F::SPLIT && !is_state) ? 0 : wave);  // index among the gate waves
   const int g_col0 = gw * F::SCOLS + 2 * (lane % F::CPG);
   const int g_rg = lane / F::CPG;
   const int g_row0 = g_rg * F::RPG;
   // Row layout (q, k, operands; operand waves): chunk row r_row, positions r_col ..
   // r_col + EPT - 1.
-  const int r_row = tid / F::TPR;
-  const int r_col = (tid % F::TPR) * F::EPT;
+  const int otid = F::SO ? jtid : tid;  // thread index among the operand waves
+  const int r_row = otid / F::TPR;
+  const int r_col = (otid % F::TPR) * F::EPT;
   // Value row layout (job waves).
   const int v_row = jtid / F::TPRV;
   const int v_col = (jtid % F::TPRV) * F::EPV;
@@ -805,33 +837,36 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   const uint32_t off_v = (uint32_t)v_row * row_bytes + (uint32_t)(vt_idx * VT + v_col) * 2;
   const uint32_t off_g = (uint32_t)g_row0 * row_bytes + (uint32_t)g_col0 * 2;
   const uint32_t off_b = (uint32_t)jtid * (uint32_t)(H * 2);
-  unsigned raw_q[F::EPT / 2], raw_k[F::EPT / 2];
-  unsigned raw_v[F::EPV / 2];
-  unsigned raw_g[F::SPASS][F::RPG];
-  unsigned raw_b = 0;
+  // Two register sets: the state-only schedule loads chunk c into set c % 2 a whole
+  // step before it is used, while the other set is being consumed; the other
+  // schedules use set 0 only.
+  unsigned raw_q[2][F::EPT / 2], raw_k[2][F::EPT / 2];
+  unsigned raw_v[2][F::EPV / 2];
+  unsigned raw_g[2][F::SPASS][F::RPG];
+  unsigned raw_b[2] = {0, 0};
   // g (gate waves), v and beta (job waves): consumed in phase A
-  auto load_g = [&](const Chunk& ck) {
+  auto load_g = [&](const Chunk& ck, int b = 0) __attribute__((always_inline)) {
     const int64_t tok_elem = (ck.tok * H + ck.h) * D;
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g + tok_elem, ck.valid * (int)row_bytes);
 #pragma unroll
     for (int ps = 0; ps < F::SPASS; ++ps)
 #pragma unroll
       for (int i = 0; i < F::RPG; ++i)
-        raw_g[ps][i] = __builtin_amdgcn_raw_buffer_load_b32(
+        raw_g[b][ps][i] = __builtin_amdgcn_raw_buffer_load_b32(
             rg, off_g + (uint32_t)i * row_bytes + 4u * F::CPG * ps, 0, 0);
   };
-  auto load_vb = [&](const Chunk& ck) {
+  auto load_vb = [&](const Chunk& ck, int b = 0) __attribute__((always_inline)) {
     const int64_t tok_elem = (ck.tok * H + ck.h) * D;
-    buf_load<F::EPV>(make_rsrc(p.v + tok_elem, ck.valid * (int)row_bytes), off_v, raw_v);
-    raw_b = __builtin_amdgcn_raw_buffer_load_b16(
+    buf_load<F::EPV>(make_rsrc(p.v + tok_elem, ck.valid * (int)row_bytes), off_v, raw_v[b]);
+    raw_b[b] = __builtin_amdgcn_raw_buffer_load_b16(
         make_rsrc(p.beta + ck.tok * H + ck.h, ck.valid * (int)H * 2), off_b, 0, 0);
   };
   // q and k: consumed in phase B
-  auto load_qk = [&](const Chunk& ck) {
+  auto load_qk = [&](const Chunk& ck, int b = 0) __attribute__((always_inline)) {
     const int64_t tok_elem = (ck.tok * H + ck.h) * D;
     const int nb = ck.valid * (int)row_bytes;
-    buf_load<F::EPT>(make_rsrc(p.q + tok_elem, nb), off_qk, raw_q);
-    buf_load<F::EPT>(make_rsrc(p.k + tok_elem, nb), off_qk, raw_k);
+    buf_load<F::EPT>(make_rsrc(p.q + tok_elem, nb), off_qk, raw_q[b]);
+    buf_load<F::EPT>(make_rsrc(p.k + tok_elem, nb), off_qk, raw_k[b]);
   };
   // Exclusive prefix over the row groups of a per-lane total t.  With four groups
   // each is one 16-lane row and the two lane swaps below combine them.  With eight
@@ -841,7 +876,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   // with the lane-swap instructions (the 16-row swap gives [r0, r0, r2, r2] and
   // [r1, r1, r3, r3]; their sum swapped across the 32-lane halves gives r0 + r1
   // to rows 2 and 3).
-  auto rowgroup_excl = [&](float t) -> float {
+  auto rowgroup_excl = [&](float t) __attribute__((always_inline)) -> float {
     if constexpr (F::RG == 4) {
       // four row groups, one per 16-lane row: the lane swaps alone combine them
       const unsigned ab = __builtin_bit_cast(unsigned, t);
@@ -866,26 +901,50 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     return in_row + ((lg & 1) ? below : 0.f) + (lg >= 2 ? lower : 0.f);
   };
   // A (gate waves): gate and inclusive prefix of the next chunk (column layout).
-  auto gate_rows = [&](Slot<F>& nxt, int nxt_valid, auto full) {
+  auto gate_rows = [&](Slot<F>& nxt, int nxt_valid, auto full, int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int ps = 0; ps < F::SPASS; ++ps) {
       const int col = g_col0 + 2 * F::CPG * ps;
+      // The sigmoids of all rows first, one instruction kind at a time (the rows are
+      // independent, so each kind's latency is covered by the other rows), then the
+      // running sums down the rows.
+      float s0[F::RPG], s1[F::RPG];
+#pragma unroll
+      for (int i = 0; i < F::RPG; ++i) {
+        s0[i] = __builtin_fmaf(bflo(raw_g[b][ps][i]), gate_mul, gate_add[ps][0]);
+        s1[i] = __builtin_fmaf(bfhi(raw_g[b][ps][i]), gate_mul, gate_add[ps][1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < F::RPG; ++i) {
+        s0[i] = __builtin_amdgcn_exp2f(s0[i]);
+        s1[i] = __builtin_amdgcn_exp2f(s1[i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < F::RPG; ++i) {
+        s0[i] = 1.0f + s0[i];
+        s1[i] = 1.0f + s1[i];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < F::RPG; ++i) {
+        s0[i] = __builtin_amdgcn_rcpf(s0[i]);
+        s1[i] = __builtin_amdgcn_rcpf(s1[i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       float run0[F::RPG], run1[F::RPG];
       float t0 = 0.f, t1 = 0.f;
 #pragma unroll
       for (int i = 0; i < F::RPG; ++i) {
-        const float z0 = __builtin_fmaf(bflo(raw_g[ps][i]), gate_mul, gate_add[ps][0]);
-        const float z1 = __builtin_fmaf(bfhi(raw_g[ps][i]), gate_mul, gate_add[ps][1]);
         if constexpr (decltype(full)::value) {
-          t0 = __builtin_fmaf(p.lb2, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z0)), t0);
-          t1 = __builtin_fmaf(p.lb2, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z1)), t1);
+          t0 = __builtin_fmaf(p.lb2, s0[i], t0);
+          t1 = __builtin_fmaf(p.lb2, s1[i], t1);
         } else {
           // no decay past the sequence; the floor only acts in one-token chunks
           const float lbv = g_row0 + i < nxt_valid ? p.lb2 : 0.f;
-          t0 += __builtin_fmaxf(lbv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z0)),
-                                p.lam2_floor);
-          t1 += __builtin_fmaxf(lbv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z1)),
-                                p.lam2_floor);
+          t0 += __builtin_fmaxf(lbv * s0[i], p.lam2_floor);
+          t1 += __builtin_fmaxf(lbv * s1[i], p.lam2_floor);
         }
         run0[i] = t0;
         run1[i] = t1;
@@ -912,59 +971,72 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   };
   // A (gate waves): gate and inclusive prefix of the next chunk (column layout);
   // a full chunk (the common case) skips the per-row end-of-sequence mask.
-  auto gate = [&](Slot<F>& nxt, int nxt_valid) {
-    if (nxt_valid == C) gate_rows(nxt, nxt_valid, std::true_type{});
-    else gate_rows(nxt, nxt_valid, std::false_type{});
+  auto gate = [&](Slot<F>& nxt, int nxt_valid, int b = 0) __attribute__((always_inline)) {
+    if (nxt_valid == C) gate_rows(nxt, nxt_valid, std::true_type{}, b);
+    else gate_rows(nxt, nxt_valid, std::false_type{}, b);
   };
   // A (job waves): value tile and beta of the next chunk.
-  auto stage_vb = [&](Slot<F>& nxt, int nxt_valid) {
-    store_words<F::EPV>(&nxt.V[v_row][v_col], raw_v);
-    if (jtid < C) nxt.beta[jtid] = jtid < nxt_valid ? fast_sigmoid(bf2f((u16)raw_b)) : 0.f;
+  auto stage_vb = [&](Slot<F>& nxt, int nxt_valid, int b = 0) __attribute__((always_inline)) {
+    store_words<F::EPV>(&nxt.V[v_row][v_col], raw_v[b]);
+    if (jtid < C) nxt.beta[jtid] = jtid < nxt_valid ? fast_sigmoid(bf2f((u16)raw_b[b])) : 0.f;
   };
   // B: norms and exponent-scaled operands of the next chunk (keys r_col ..
   // r_col + EPT - 1 of chunk row r_row).
-  auto prep_B = [&](Slot<F>& nxt) {
+  auto prep_B = [&](Slot<F>& nxt, int b = 0) __attribute__((always_inline)) {
+    // The prefix, offset and end factor of every position are read first (LDS reads
+    // only, in flight while the norms reduce); then each arithmetic kind runs over all
+    // positions, so the positions cover each other's latency; then the stores.
+    constexpr int NG = F::EPT / 4;
+    f32x4_t gg[NG], go[NG], tt[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const int key = r_col + 4 * j;
+      gg[j] = *reinterpret_cast<const f32x4_t*>(&sm.G[r_row][key]);
+      go[j] = *reinterpret_cast<const f32x4_t*>(&sm.Goff[r_row / F::RPG][key]);
+      tt[j] = *reinterpret_cast<const f32x4_t*>(&sm.gtc[key]);
+    }
     float qn[F::EPT], kn[F::EPT];
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int w = 0; w < F::EPT / 2; ++w) {
-      qn[2 * w] = bflo(raw_q[w]); qn[2 * w + 1] = bfhi(raw_q[w]);
-      kn[2 * w] = bflo(raw_k[w]); kn[2 * w + 1] = bfhi(raw_k[w]);
-      sq = dot2_bf16(raw_q[w], raw_q[w], sq);
-      sk = dot2_bf16(raw_k[w], raw_k[w], sk);
+      qn[2 * w] = bflo(raw_q[b][w]); qn[2 * w + 1] = bfhi(raw_q[b][w]);
+      kn[2 * w] = bflo(raw_k[b][w]); kn[2 * w + 1] = bfhi(raw_k[b][w]);
+      sq = dot2_bf16(raw_q[b][w], raw_q[b][w], sq);
+      sk = dot2_bf16(raw_k[b][w], raw_k[b][w], sk);
     }
     sq = group_sum<F::TPR>(sq);
     sk = group_sum<F::TPR>(sk);
     const float rq = __builtin_amdgcn_rsqf(sq + kNormEps);
     const float rk = __builtin_amdgcn_rsqf(sk + kNormEps);
+    float e1[F::EPT], e2[F::EPT];
+#pragma unroll
+    for (int x = 0; x < F::EPT; ++x) e1[x] = gg[x / 4][x % 4] + go[x / 4][x % 4];  // G - Ca
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int x = 0; x < F::EPT; ++x) {
+      e2[x] = __builtin_amdgcn_exp2f(-e1[x]);  // 2^(Ca - G)
+      e1[x] = __builtin_amdgcn_exp2f(e1[x]);   // 2^(G - Ca)
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float oQc[F::EPT], oKc[F::EPT], oKi[F::EPT], oKr[F::EPT];
+#pragma unroll
+    for (int x = 0; x < F::EPT; ++x) {
+      const float qv = qn[x] * rq, kv = kn[x] * rk;
+      oQc[x] = qv * e1[x];
+      oKc[x] = kv * e1[x];
+      oKi[x] = kv * e2[x];
+      oKr[x] = oKi[x] * tt[x / 4][x % 4];  // kh 2^(G_T - G)
+    }
     // eight positions (one 16-byte store per operand) at a time
     constexpr int RUN = F::EPT < 8 ? F::EPT : 8;
 #pragma unroll
     for (int r0 = 0; r0 < F::EPT; r0 += RUN) {
-      float oQc[RUN], oKc[RUN], oKi[RUN], oKr[RUN];
 #pragma unroll
-      for (int j = 0; j < RUN / 4; ++j) {
-        const int key = r_col + r0 + 4 * j;
-        const f32x4_t gg = *reinterpret_cast<const f32x4_t*>(&sm.G[r_row][key]);
-        const f32x4_t go = *reinterpret_cast<const f32x4_t*>(&sm.Goff[r_row / F::RPG][key]);
-        const f32x4_t tt = *reinterpret_cast<const f32x4_t*>(&sm.gtc[key]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int x = 4 * j + e;
-          const float qv = qn[r0 + x] * rq, kv = kn[r0 + x] * rk;
-          const float d = gg[e] + go[e];                // G - Ca
-          const float e1 = __builtin_amdgcn_exp2f(d);   // 2^(G - Ca)
-          const float e2 = __builtin_amdgcn_exp2f(-d);  // 2^(Ca - G)
-          oQc[x] = qv * e1;
-          oKc[x] = kv * e1;
-          oKi[x] = kv * e2;
-          oKr[x] = oKi[x] * tt[e];                      // kh 2^(G_T - G)
-        }
-        store_bf16<4>(&nxt.Kr[r_row][row_of_key(key)], &oKr[4 * j]);
-      }
-      store_bf16<RUN>(&sm.Qc[r_row][r_col + r0], oQc);
-      store_bf16<RUN>(&sm.Kc[r_row][r_col + r0], oKc);
-      store_bf16<RUN>(&sm.Ki[r_row][r_col + r0], oKi);
+      for (int j = 0; j < RUN / 4; ++j)
+        store_bf16<4>(&nxt.Kr[r_row][row_of_key(r_col + r0 + 4 * j)], &oKr[r0 + 4 * j]);
+      store_bf16<RUN>(&qc_of(nxt)[r_row][r_col + r0], &oQc[r0]);
+      store_bf16<RUN>(&kc_of(nxt)[r_row][r_col + r0], &oKc[r0]);
+      store_bf16<RUN>(&sm.Ki[r_row][r_col + r0], &oKi[r0]);
     }
   };
   // A: the chunk-local matrices of the current chunk from its centred operands,
@@ -972,9 +1044,9 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   //   L tiles:   L = strictLower(diag(beta) Kc Ki^T); a diagonal tile is inverted
   //              on the spot (X = (I + L)^-1), the lower-left tile is kept as -L21;
   //   Mqk tiles: lowerTri(Qc Ki^T).
-  auto tile = [&](Slot<F>& cur, bool is_l, int ti, int tj) {
+  auto tile = [&](Slot<F>& cur, bool is_l, int ti, int tj) __attribute__((always_inline)) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    const u16* arow = is_l ? &sm.Kc[16 * ti + l16][0] : &sm.Qc[16 * ti + l16][0];
+    const u16* arow = is_l ? &kc_of(cur)[16 * ti + l16][0] : &qc_of(cur)[16 * ti + l16][0];
     const u16* brow = &sm.Ki[16 * tj + l16][0];
 #pragma unroll
     for (int ks = 0; ks < F::KS; ++ks)
@@ -1032,19 +1104,28 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) cur.SOL[base + gq + 4 * t][base + m] = to_bf16(kStateDown * x[t]);
   };
-  auto chunk_matrices = [&](Slot<F>& cur) {
-    if constexpr (F::CT == 2) {
+  // Matrix job j of a 32-token chunk: 0 L00, 1 L11 (each with its inversion), 2 L10,
+  // 3 Mqk10, 4 Mqk00, 5 Mqk11.
+  auto tile_job = [&](Slot<F>& cur, int j) __attribute__((always_inline)) {
+    switch (j) {
+      case 0: tile(cur, true, 0, 0); break;
+      case 1: tile(cur, true, 1, 1); break;
+      case 2: tile(cur, true, 1, 0); break;
+      case 3: tile(cur, false, 1, 0); break;
+      case 4: tile(cur, false, 0, 0); break;
+      default: tile(cur, false, 1, 1); break;
+    }
+  };
+  auto chunk_matrices = [&](Slot<F>& cur) __attribute__((always_inline)) {
+    if constexpr (F::SO) {
+      // the state-only schedule: the two inversions on job waves 0 and 1; the other
+      // four tiles run on the state waves after their state update
+      if (jw < 2) tile_job(cur, jw);
+    } else if constexpr (F::CT == 2) {
 #pragma unroll
       for (int j = 0; j < 6; ++j) {
         if (job_wave<F::NJW, 2>(j) != jw) continue;  // uniform
-        switch (j) {
-          case 0: tile(cur, true, 0, 0); break;
-          case 1: tile(cur, true, 1, 1); break;
-          case 2: tile(cur, true, 1, 0); break;
-          case 3: tile(cur, false, 1, 0); break;
-          case 4: tile(cur, false, 0, 0); break;
-          default: tile(cur, false, 1, 1); break;
-        }
+        tile_job(cur, j);
       }
     } else {
       if (job_wave<F::NJW, 1>(0) == jw) tile(cur, true, 0, 0);
@@ -1067,8 +1148,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   auto rec_lds = [&](Slot<F>& sl, int u) -> u32x4_t* {
     char* b;
     int o;
-    if (u < kQU) { b = reinterpret_cast<char*>(&sm.Qc[0][0]); o = u; }
-    else if (u < 2 * kQU) { b = reinterpret_cast<char*>(&sm.Kc[0][0]); o = u - kQU; }
+    if (u < kQU) { b = reinterpret_cast<char*>(&qc_of(sl)[0][0]); o = u; }
+    else if (u < 2 * kQU) { b = reinterpret_cast<char*>(&kc_of(sl)[0][0]); o = u - kQU; }
     else if (u < 2 * kQU + kRU) { b = reinterpret_cast<char*>(&sl.Kr[0][0]); o = u - 2 * kQU; }
     else if (u < 2 * kQU + kRU + kCU) {
       b = reinterpret_cast<char*>(&sl.SOL[0][0]);
@@ -1115,11 +1196,11 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   };
   // beta alone (the prep kernel does not stage values)
   auto load_b = [&](const Chunk& ck) {
-    raw_b = __builtin_amdgcn_raw_buffer_load_b16(
+    raw_b[0] = __builtin_amdgcn_raw_buffer_load_b16(
         make_rsrc(p.beta + ck.tok * H + ck.h, ck.valid * (int)H * 2), off_b, 0, 0);
   };
   auto stage_b = [&](Slot<F>& nxt, int nxt_valid) {
-    if (jtid < C) nxt.beta[jtid] = jtid < nxt_valid ? fast_sigmoid(bf2f((u16)raw_b)) : 0.f;
+    if (jtid < C) nxt.beta[jtid] = jtid < nxt_valid ? fast_sigmoid(bf2f((u16)raw_b[0])) : 0.f;
   };
 
   // ======================= schedule ==========================================
@@ -1184,6 +1265,81 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
           load_rec(nxt2);
         }
         lds_barrier();
+      }
+    }
+  } else if constexpr (F::SO) {
+    // State-only schedule.  Step s: the state waves run chunk s (A: P, O0, the decay
+    // and R; B: the solve, the state update and the output, then four of chunk s+1's
+    // matrix tiles).  The job waves work one chunk further ahead: A: norms, operands
+    // and value tile of chunk s+1; B: the two inverted tiles of chunk s+1 and the
+    // gate and prefix of chunk s+2.  Three fill phases come first (gate of chunk 0;
+    // its operands; its matrices and the gate of chunk 1); every wave passes the same
+    // barriers.
+    if (is_state) {
+      state_in(sbase0);
+      state_cvt();
+      if (nchunks > 0) {
+        lds_barrier();
+        lds_barrier();
+        tile_job(sm.slot[0], 2 + wave);
+        lds_barrier();
+        for (int s = 0; s < nchunks; ++s) {
+          Slot<F>& cur = sm.slot[s & 1];
+          state_A(cur);
+          state_R(cur);
+          lds_barrier();
+          state_B(cur, ck(s));
+          if (s + 1 < nchunks) tile_job(sm.slot[(s + 1) & 1], 2 + wave);
+          lds_barrier();
+        }
+      }
+      state_out(sbase0);
+    } else if (nchunks > 0) {
+      // Raw inputs of chunk c go to register set c % 2, loaded at the start of the
+      // phase a whole step before they are used.
+      const int c2nd = nchunks > 2 ? 2 : nchunks - 1;
+      if (is_gate) load_g(ck(0), 0);
+      load_vb(ck(0), 0);
+      load_qk(ck(0), 0);
+      if (is_gate) load_g(ck(c1st), 1);
+      load_vb(ck(c1st), 1);
+      load_qk(ck(c1st), 1);
+      if (is_gate) gate(sm.slot[0], chunk_valid(0), 0);
+      stage_vb(sm.slot[0], chunk_valid(0), 0);
+      lds_barrier();
+      prep_B(sm.slot[0], 0);
+      lds_barrier();
+      if (is_gate) load_g(ck(c2nd), 0);
+      chunk_matrices(sm.slot[0]);
+      if (is_gate && nchunks > 1) gate(sm.slot[1], chunk_valid(1), 1);
+      lds_barrier();
+      // one step; b = s % 2 is a compile-time constant in the unrolled loop below
+      auto job_step = [&](int s, auto par) __attribute__((always_inline)) {
+        constexpr int b = decltype(par)::value;
+        Slot<F>& nxt = sm.slot[(s + 1) & 1];
+        const bool more = s + 1 < nchunks;   // uniform
+        const bool more2 = s + 2 < nchunks;  // uniform
+        const int n2 = more2 ? s + 2 : nchunks - 1;
+        const int n3 = s + 3 < nchunks ? s + 3 : nchunks - 1;
+        load_qk(ck(n2), b);
+        load_vb(ck(n2), b);
+        if (more) {
+          prep_B(nxt, 1 - b);
+          stage_vb(nxt, chunk_valid(s + 1), 1 - b);
+        }
+        lds_barrier();
+        if (is_gate) load_g(ck(n3), 1 - b);
+        if (more) chunk_matrices(nxt);
+        if (more2 && is_gate) {
+          // chunk s+2 goes to slot s % 2: its decay vector replaces chunk s's, which
+          // the state waves read in phase A
+          gate(sm.slot[s & 1], chunk_valid(s + 2), b);
+        }
+        lds_barrier();
+      };
+      for (int s = 0; s < nchunks; s += 2) {
+        job_step(s, std::integral_constant<int, 0>{});
+        if (s + 1 < nchunks) job_step(s + 1, std::integral_constant<int, 1>{});
       }
     }
   } else if constexpr (F::SPLIT) {
@@ -1310,7 +1466,7 @@ hipError_t launch_one(const KdaParams& p, hipStream_t stream) {
 
 // (D, chunk, value tile, waves, state waves)
 #define KDA_SCHEDULES(X)  \
-  X(128, 32, 128, 8, 4)   \
+  X(128, 32, 128, 12, 4)  \
   X(128, 16, 128, 8, 4)   \
   X(128, 32, 64, 8, 4)    \
   X(128, 16, 64, 4, 4)    \

@@ -192,7 +192,7 @@ int kda_fwd_transposed_state(const void* q, const void* k, const void* v, const 
  *   lower_bound, chunk_size  as for kda_fwd_sched (0: automatic chunk length).
  * One record per slot and head: the prepared operands of one chunk (Qc, Kc, Kr,
  * the solve operands, Mqk and the decay, in the layout the recurrent kernel copies
- * into LDS; 32,256 bytes at 32-token chunks).  A head has floor(T_total / chunk)
+ * into LDS; 33,280 bytes at 32-token chunks).  A head has floor(T_total / chunk)
  * + num_seqs + 1 slots.  Returns the size, or a negative status
  * (KDA_ERR_BAD_SHAPE, KDA_ERR_BAD_LOWER_BOUND, KDA_ERR_BAD_SCHEDULE).
  */
