@@ -213,7 +213,7 @@ def main():
             sys.exit(2)
         ws_bytes = kda.kda_split_workspace_bytes(B * T, args_c[15], H, D, w.lower_bound, 0)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-        call = lambda: lib.kda_fwd_split(*args_c, ws.data_ptr(), ws_bytes, int(args.v_tile))
+        call = lambda: lib.kda_fwd_split(*args_c, ws.data_ptr(), ws_bytes, 0, int(args.v_tile))
     elif order is not None:
         call = lambda: lib.kda_fwd_ordered(*args_c, order.data_ptr())
     else:

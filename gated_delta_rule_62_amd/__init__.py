@@ -71,7 +71,7 @@ def load_library():
     lib.kda_longest_first.restype = i32
     lib.kda_split_workspace_bytes.argtypes = [i64, i64, i64, i64, f32, i32]
     lib.kda_split_workspace_bytes.restype = i64
-    lib.kda_fwd_split.argtypes = common + [vp, vp, i64, i32]
+    lib.kda_fwd_split.argtypes = common + [vp, vp, i64, i32, i32]
     lib.kda_fwd_split.restype = i32
     lib.kda_fwd_check.argtypes = common + [i32, i32]
     lib.kda_fwd_check.restype = i32
@@ -225,11 +225,12 @@ def kda_split_workspace_bytes(T_total: int, num_seqs: int, H: int, D: int, lower
 
 def kda_fwd_split(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, workspace,
                   initial_state=None, final_state=None, cu_seqlens=None, v_tile: int = 0,
-                  stream=None) -> None:
+                  stream=None, chunk_size: int = 0) -> None:
     """``kda_fwd`` as two kernels: a token-parallel preparation of every chunk into
-    ``workspace`` (a contiguous uint8 device tensor of at least ``kda_split_workspace_bytes``
-    bytes), then the recurrent kernel on value tiles of ``v_tile`` rows (0: automatic).
-    The results are bitwise those of ``kda_fwd_sched`` with the same value tile."""
+    ``workspace`` (a contiguous uint8 device tensor of at least
+    ``kda_split_workspace_bytes(..., chunk_size)`` bytes), then the recurrent kernel on
+    value tiles of ``v_tile`` rows (0: automatic).  The results are bitwise those of
+    ``kda_fwd_sched`` with the same chunk length and value tile."""
     import torch
     if workspace.dtype != torch.uint8 or workspace.dim() != 1:
         raise ValueError("workspace must be a 1-d uint8 tensor")
@@ -237,7 +238,7 @@ def kda_fwd_split(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, wor
                   final_state, cu_seqlens, stream, extra=(workspace,))
     with _on_device(q):
         st = load_library().kda_fwd_split(*args, workspace.data_ptr(), workspace.numel(),
-                                          int(v_tile))
+                                          int(chunk_size), int(v_tile))
     if st != KDA_OK:
         raise KdaError(st)
 

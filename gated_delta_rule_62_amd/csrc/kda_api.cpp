@@ -121,6 +121,12 @@ int resolve(const void* q, const void* k, const void* v, const void* g, const vo
   const int tile = tile_rows(chunk);
   int vt = v_tile == 0 ? auto_v_tile(D, tile, num_seqs * H) : v_tile;
   if (!kda::kda_schedule_supported(static_cast<int>(D), tile, vt)) return KDA_ERR_BAD_SCHEDULE;
+  // One launch covers at most 2^32 - 1 work-items: workgroups (units rounded up to
+  // groups of eight when a unit has several value tiles) times their threads.
+  const int64_t tiles = D / vt;
+  const int64_t groups = tiles == 1 ? num_seqs * H : (num_seqs * H + 7) / 8 * 8 * tiles;
+  if (groups > (((int64_t)1 << 32) - 1) / kda::kda_schedule_threads(static_cast<int>(D), tile, vt))
+    return KDA_ERR_BAD_SHAPE;
 
   // Buffer extents and the aliasing contract.
   const int64_t tok = B * T;
@@ -159,6 +165,8 @@ int64_t split_head_bytes(int64_t T_total, int64_t num_seqs, int64_t H, int64_t D
   const int64_t rec = kda::kda_record_bytes(D, tile_rows(chunk));
   if (slots > (((int64_t)1 << 31) - 1) / rec || slots > (((int64_t)1 << 31) - 1) / H)
     return KDA_ERR_BAD_SHAPE;
+  // the prep kernel's grid (one workgroup per slot and head) stays below 2^32 work-items
+  if (slots * H > (((int64_t)1 << 32) - 1) / kda::kSplitPrepThreads) return KDA_ERR_BAD_SHAPE;
   return slots * rec;
 }
 
@@ -337,10 +345,10 @@ int kda_fwd_split(const void* q, const void* k, const void* v, const void* g, co
                   float lower_bound, const void* initial_state, int initial_state_dtype,
                   void* final_state, int final_state_dtype, const int64_t* cu_seqlens,
                   int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t D, void* stream,
-                  void* workspace, int64_t workspace_bytes, int v_tile) {
+                  void* workspace, int64_t workspace_bytes, int chunk_size, int v_tile) {
   return launch(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                 initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T,
-                H, D, stream, 0, v_tile, nullptr, 0, true, workspace, workspace_bytes);
+                H, D, stream, chunk_size, v_tile, nullptr, 0, true, workspace, workspace_bytes);
 }
 
 float kda_chunk_anchor(float lower_bound, int chunk_size) {

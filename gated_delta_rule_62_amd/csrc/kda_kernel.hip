@@ -1526,12 +1526,14 @@ hipError_t launch_longest_first(const int64_t* cu, int num_seqs, int32_t* order,
   return hipGetLastError();
 }
 
-bool kda_schedule_supported(int D, int chunk, int v_tile) {
-#define KDA_SUPPORTED(d, c, vt, nw, nsw) \
-  if (D == d && chunk == c && v_tile == vt) return true;
-  KDA_SCHEDULES(KDA_SUPPORTED)
-#undef KDA_SUPPORTED
-  return false;
+bool kda_schedule_supported(int D, int chunk, int v_tile) { return kda_schedule_threads(D, chunk, v_tile) > 0; }
+
+int kda_schedule_threads(int D, int chunk, int v_tile) {
+#define KDA_THREADS(d, c, vt, nw, nsw) \
+  if (D == d && chunk == c && v_tile == vt) return nw * 64;
+  KDA_SCHEDULES(KDA_THREADS)
+#undef KDA_THREADS
+  return 0;
 }
 
 // The split's schedules: (D, chunk, value tile, waves, state waves) of the

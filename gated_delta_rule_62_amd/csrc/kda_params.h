@@ -63,6 +63,12 @@ hipError_t launch_kda_fwd(const KdaParams& p, int D, int chunk, int v_tile, hipS
 // Whether a (D, chunk, v_tile) schedule has a compiled kernel.
 bool kda_schedule_supported(int D, int chunk, int v_tile);
 
+// Threads per workgroup of a compiled (D, chunk, v_tile) schedule, 0 if none.
+int kda_schedule_threads(int D, int chunk, int v_tile);
+
+// Threads per workgroup of the split's prep kernel.
+constexpr int kSplitPrepThreads = 512;
+
 // The two-kernel split: a token-parallel kernel writes every chunk's record into
 // p.ws, then the recurrent kernel reads them back (same schedule as the fused
 // kernel).  Both are enqueued on `stream`; returns a hipError_t.

@@ -51,8 +51,10 @@ extern "C" {
                                      /* out may be NULL when B * T == 0)                */
 #define KDA_ERR_BAD_SHAPE (-2)       /* B,T,H < 1 (T may be 0 only with cu_seqlens),     */
                                      /* D not in {32, 64, 128}, H * D >= 2^25,            */
-                                     /* B * T > 2^40, num_seqs * H > 2^29, or an          */
-                                     /* activation tensor of more than 2^62 bytes         */
+                                     /* B * T > 2^40, num_seqs * H > 2^29, an activation  */
+                                     /* tensor of more than 2^62 bytes, or a launch of    */
+                                     /* more than 2^32 - 1 work-items (workgroups times   */
+                                     /* their 128 to 768 threads)                         */
 #define KDA_ERR_BAD_DTYPE (-3)       /* unknown state dtype code                         */
 #define KDA_ERR_BAD_VARLEN (-4)      /* cu_seqlens with B != 1, num_seqs < 1, or         */
                                      /* num_seqs != B without cu_seqlens                 */
@@ -189,12 +191,15 @@ int kda_fwd_transposed_state(const void* q, const void* k, const void* v, const 
  *   T_total     tokens of the flattened batch (B * T).
  *   num_seqs    N, as for kda_fwd.
  *   H, D        heads and head dimension; the split runs D = 128 only.
- *   lower_bound, chunk_size  as for kda_fwd_sched (0: automatic chunk length).
+ *   lower_bound, chunk_size  as for kda_fwd_sched (0: automatic chunk length); pass
+ *               kda_fwd_split the same chunk_size.
  * One record per slot and head: the prepared operands of one chunk (Qc, Kc, Kr,
  * the solve operands, Mqk and the decay, in the layout the recurrent kernel copies
  * into LDS; 33,280 bytes at 32-token chunks).  A head has floor(T_total / chunk)
  * + num_seqs + 1 slots.  Returns the size, or a negative status
- * (KDA_ERR_BAD_SHAPE, KDA_ERR_BAD_LOWER_BOUND, KDA_ERR_BAD_SCHEDULE).
+ * (KDA_ERR_BAD_SHAPE, also when a head's records reach 2^31 bytes or the prep
+ * kernel's grid of slots times heads workgroups of 512 threads exceeds 2^32 - 1
+ * work-items; KDA_ERR_BAD_LOWER_BOUND; KDA_ERR_BAD_SCHEDULE).
  */
 int64_t kda_split_workspace_bytes(int64_t T_total, int64_t num_seqs, int64_t H, int64_t D,
                                   float lower_bound, int chunk_size);
@@ -208,14 +213,17 @@ int64_t kda_split_workspace_bytes(int64_t T_total, int64_t num_seqs, int64_t H, 
  * `workspace`.  The recurrent kernel then reads those records back in chunk order
  * and runs only the state side, on value tiles of v_tile rows.
  *   workspace        caller-owned device memory of at least
- *                    kda_split_workspace_bytes(B * T, num_seqs, H, D, lower_bound, 0)
- *                    bytes (KDA_ERR_BAD_WORKSPACE otherwise, KDA_ERR_NULL_ARG when NULL).
- *                    It must not overlap any other argument (KDA_ERR_BAD_ALIAS).  Its
- *                    contents on entry do not matter and are scratch on return.
+ *                    kda_split_workspace_bytes(B * T, num_seqs, H, D, lower_bound,
+ *                    chunk_size) bytes (KDA_ERR_BAD_WORKSPACE otherwise,
+ *                    KDA_ERR_NULL_ARG when NULL).  It must not overlap any other
+ *                    argument (KDA_ERR_BAD_ALIAS).  Its contents on entry do not
+ *                    matter and are scratch on return.
  *   workspace_bytes  its size in bytes.
+ *   chunk_size       0 (automatic) or a forced chunk length, as for kda_fwd_sched.
  *   v_tile           0 (automatic, as for kda_fwd), 128, or 64 at 32-token chunks;
  *                    other schedules are KDA_ERR_BAD_SCHEDULE, as is D != 128.
- * The results are bitwise those of kda_fwd_sched with the same value tile: both
+ * The results are bitwise those of kda_fwd_sched with the same chunk length and
+ * value tile: both
  * kernels run the fused kernel's own preparation and state-side code.  Both are
  * enqueued on `stream`.  Everything else is exactly as kda_fwd.
  */
@@ -224,7 +232,7 @@ int kda_fwd_split(const void* q, const void* k, const void* v, const void* g, co
                   float lower_bound, const void* initial_state, int initial_state_dtype,
                   void* final_state, int final_state_dtype, const int64_t* cu_seqlens,
                   int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t D, void* stream,
-                  void* workspace, int64_t workspace_bytes, int v_tile);
+                  void* workspace, int64_t workspace_bytes, int chunk_size, int v_tile);
 
 /*
  * kda_longest_first -- writes the longest-first order of a packed batch for

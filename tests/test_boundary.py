@@ -130,8 +130,10 @@ def test_size_limits_reject_without_overflow(lib):
     assert _check(B=1, T=1 << 37, H=1 << 19, D=32) != bad        # exactly 2^62 bytes
     assert _check(B=1, T=100, N=1 << 62, has_cu=True) == bad     # num_seqs H overflows
     assert _check(B=1, T=100, N=(1 << 27) + 1, H=4, has_cu=True) == bad
+    # num_seqs H = 2^29 passes the unit-count bound but is far beyond the work-item
+    # limit of one launch (test_launch_work_item_limit)
     assert _check(B=1, T=100, N=1 << 27, H=4, has_cu=True, has_s_in=False,
-                  has_s_out=False) == kda.KDA_OK                 # num_seqs H = 2^29
+                  has_s_out=False) == bad
 
 
 def test_dtype_and_varlen_errors(lib):
@@ -245,11 +247,18 @@ def test_split_workspace_bytes(lib):
     # a head's records must stay below 2^31 bytes (31-bit offsets)
     assert raw(1 << 22, 1, 1, 128, -5.0, 0) == kda.KDA_ERR_BAD_SHAPE
     assert raw(1 << 20, 1, 1, 128, -5.0, 0) == ((1 << 15) + 2) * rec32
+    # the sizing the library computes is floor(T_total / chunk) + N + 1 records per head
+    rng = random.Random(11)
+    for _ in range(200):
+        T, N, H = rng.randint(0, 5000), rng.randint(1, 40), rng.randint(1, 97)
+        chunk = rng.choice([32, 16, 8, 4, 2, 1])
+        rec = rec32 if chunk == 32 else rec16
+        assert raw(T, N, H, 128, -0.5, chunk) == (T // chunk + N + 1) * rec * H
 
 
-def _split(ws, ws_bytes, vt=0, **kw):
+def _split(ws, ws_bytes, vt=0, chunk=0, **kw):
     a = _args(**kw)
-    return kda.load_library().kda_fwd_split(*a[:-2], None, ws, ws_bytes, vt)
+    return kda.load_library().kda_fwd_split(*a[:-2], None, ws, ws_bytes, chunk, vt)
 
 
 def test_split_validation(lib):
@@ -268,6 +277,37 @@ def test_split_validation(lib):
     # everything kda_fwd rejects is still rejected
     assert _split(12 * GB, need, lb=1.0) == kda.KDA_ERR_BAD_LOWER_BOUND
     assert _split(12 * GB, need, q=None) == kda.KDA_ERR_NULL_ARG
+    # a forced chunk length sizes and runs the same split: a workspace sized for
+    # 16-token chunks is enough with chunk_size 16 (the call then reaches the alias
+    # check, which follows the size check) and too small for the automatic 32
+    need16 = kda.kda_split_workspace_bytes(2 * 64, 2, 4, 128, -5.0, 16)
+    assert need16 < need
+    assert _split(1 * GB, need16, chunk=16) == kda.KDA_ERR_BAD_ALIAS
+    assert _split(1 * GB, need16, chunk=0) == kda.KDA_ERR_BAD_WORKSPACE
+    assert _split(12 * GB, need, chunk=24) == kda.KDA_ERR_BAD_SCHEDULE
+    assert _split(12 * GB, need, chunk=32, lb=-6.0) == kda.KDA_ERR_BAD_LOWER_BOUND
+
+
+def test_launch_work_item_limit():
+    """A launch covers at most 2^32 - 1 work-items: workgroups times their threads.
+    D = 32 runs 128-thread workgroups (one per sequence and head); D = 128 with
+    32-token chunks and value tile 128 runs 768-thread ones.  The split's prep kernel
+    runs one 512-thread workgroup per slot and head."""
+    ok = kda.KDA_OK
+    packed = dict(B=1, T=8, H=1, has_cu=True, has_s_in=False, has_s_out=False)
+    lim32 = ((1 << 32) - 1) // 128
+    assert _check(N=lim32, D=32, **packed) == ok
+    assert _check(N=lim32 + 1, D=32, **packed) == kda.KDA_ERR_BAD_SHAPE
+    lim128 = ((1 << 32) - 1) // 768
+    assert _check(N=lim128, D=128, vt=128, **packed) == ok
+    assert _check(N=lim128 + 1, D=128, vt=128, **packed) == kda.KDA_ERR_BAD_SHAPE
+    ws = kda.load_library().kda_split_workspace_bytes
+    limp = ((1 << 32) - 1) // 512
+    H = 1 << 10
+    slots_ok = limp // H                      # 8191 slots of one sequence
+    t_ok = (slots_ok - 2) * 32
+    assert ws(t_ok, 1, H, 128, -5.0, 0) > 0
+    assert ws(t_ok + 32, 1, H, 128, -5.0, 0) == kda.KDA_ERR_BAD_SHAPE
 
 
 def test_split_slot_numbering_is_injective_and_fits():

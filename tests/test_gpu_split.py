@@ -31,8 +31,8 @@ def _workspace(inp, w, fill=0xFF):
 
 
 def _run_both(w, vt=0, inplace=False):
-    # the split takes the automatic chunk length; so does the fused run it is compared with
-    assert w.chunk_size == 0
+    # both runs take the workload's chunk length (0: automatic)
+    chunk = w.chunk_size
     print("case: %s B=%d T=%d H=%d lengths=%s lb=%g state %s->%s vt=%d inplace=%s"
           % (w.name, w.B, w.T, w.H, w.lengths, w.lower_bound, w.state_in, w.state_out, vt,
              inplace), flush=True)
@@ -45,14 +45,16 @@ def _run_both(w, vt=0, inplace=False):
     s0 = inp["initial_state"]
     if inplace:
         st_f, st_s = s0.clone(), s0.clone()
-        kda.kda_fwd_sched(*args, out_f, *tail, st_f, st_f, inp["cu_seqlens"], 0, vt)
-        kda.kda_fwd_split(*args, out_s, *tail, ws, st_s, st_s, inp["cu_seqlens"], vt)
+        kda.kda_fwd_sched(*args, out_f, *tail, st_f, st_f, inp["cu_seqlens"], chunk, vt)
+        kda.kda_fwd_split(*args, out_s, *tail, ws, st_s, st_s, inp["cu_seqlens"], vt,
+                          chunk_size=chunk)
         fin_f, fin_s = st_f, st_s
     else:
         fin_f = None if inp["final_state"] is None else torch.full_like(inp["final_state"], 7.0)
         fin_s = None if fin_f is None else torch.full_like(fin_f, 7.0)
-        kda.kda_fwd_sched(*args, out_f, *tail, s0, fin_f, inp["cu_seqlens"], 0, vt)
-        kda.kda_fwd_split(*args, out_s, *tail, ws, s0, fin_s, inp["cu_seqlens"], vt)
+        kda.kda_fwd_sched(*args, out_f, *tail, s0, fin_f, inp["cu_seqlens"], chunk, vt)
+        kda.kda_fwd_split(*args, out_s, *tail, ws, s0, fin_s, inp["cu_seqlens"], vt,
+                          chunk_size=chunk)
     torch.cuda.synchronize()
     return inp, out_f, out_s, fin_f, fin_s
 
@@ -75,6 +77,18 @@ def test_split_equals_fused_on_the_workloads(name, vt):
     _bitwise(out_s, out_f, "out")
     if fin_f is not None:
         _bitwise(fin_s, fin_f, "final_state")
+
+
+@pytest.mark.parametrize("chunk", [16, 8, 1])
+def test_split_forced_chunk_equals_fused(chunk):
+    """A forced chunk length (as kda_fwd_sched takes it) sizes the workspace and runs both
+    split kernels with it: packed sequences around the chunk lengths, lb = -5."""
+    w = Workload("packed_forced_%d" % chunk, B=1, T=0, H=3, D=128, seed=61,
+                 lengths=[0, 1, 17, 40, 0, 9], state_in="fp32", state_out="bf16",
+                 chunk_size=chunk)
+    _, out_f, out_s, fin_f, fin_s = _run_both(w, 0)
+    _bitwise(out_s, out_f, "out")
+    _bitwise(fin_s, fin_f, "final_state")
 
 
 def test_split_equals_fused_long_two_value_tiles():
