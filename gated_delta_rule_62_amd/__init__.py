@@ -14,7 +14,7 @@ import os
 from ._build import LIB_PATH, build  # noqa: F401  (build() is the in-tree compile step)
 
 __all__ = ["kda_fwd", "kda_fwd_sched", "kda_fwd_ordered", "kda_fwd_transposed_state",
-           "kda_fwd_split", "kda_split_workspace_bytes",
+           "kda_fwd_split", "kda_split_workspace_bytes", "kda_fwd_split_noalloc",
            "kda_longest_first", "kda_fwd_check", "c_args",
            "kda_chunk_anchor", "kda_status_string", "KdaError", "library_path", "load_library"]
 
@@ -29,6 +29,7 @@ KDA_ERR_BAD_SCALE = -7
 KDA_ERR_BAD_SCHEDULE = -8
 KDA_ERR_HIP = -9
 KDA_ERR_BAD_WORKSPACE = -10
+KDA_ERR_SCRATCH_TOO_SMALL = -11
 KDA_DTYPE_BF16 = 0
 KDA_DTYPE_FP32 = 1
 
@@ -72,6 +73,10 @@ def load_library():
     lib.kda_split_workspace_bytes.argtypes = [i64, i64, i64, i64, f32, i32]
     lib.kda_split_workspace_bytes.restype = i64
     lib.kda_fwd_split.argtypes = common + [vp, vp, i64, i32, i32]
+    lib.kda_fwd_split_noalloc.argtypes = common + [vp, i32, i32]
+    lib.kda_fwd_split_noalloc.restype = i32
+    lib.kda_split_noalloc_max_bytes.argtypes = []
+    lib.kda_split_noalloc_max_bytes.restype = i64
     lib.kda_fwd_split.restype = i32
     lib.kda_fwd_check.argtypes = common + [i32, i32]
     lib.kda_fwd_check.restype = i32
@@ -239,6 +244,20 @@ def kda_fwd_split(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, wor
     with _on_device(q):
         st = load_library().kda_fwd_split(*args, workspace.data_ptr(), workspace.numel(),
                                           int(chunk_size), int(v_tile))
+    if st != KDA_OK:
+        raise KdaError(st)
+
+
+def kda_fwd_split_noalloc(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                          initial_state=None, final_state=None, cu_seqlens=None,
+                          v_tile: int = 0, stream=None, chunk_size: int = 0) -> None:
+    """``kda_fwd_split`` with the library's per-GPU static scratch as its workspace (for
+    callers that cannot allocate); raises ``KdaError(KDA_ERR_SCRATCH_TOO_SMALL)`` when
+    the call's workspace would exceed it."""
+    args = c_args(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                  final_state, cu_seqlens, stream)
+    with _on_device(q):
+        st = load_library().kda_fwd_split_noalloc(*args, int(chunk_size), int(v_tile))
     if st != KDA_OK:
         raise KdaError(st)
 

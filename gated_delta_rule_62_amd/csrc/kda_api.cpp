@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/kda.h"
 #include "kda_params.h"
@@ -168,6 +169,31 @@ int64_t split_head_bytes(int64_t T_total, int64_t num_seqs, int64_t H, int64_t D
   // the prep kernel's grid (one workgroup per slot and head) stays below 2^32 work-items
   if (slots * H > (((int64_t)1 << 32) - 1) / kda::kSplitPrepThreads) return KDA_ERR_BAD_SHAPE;
   return slots * rec;
+}
+
+// Scratch of kda_fwd_split_noalloc: the split's workspace in a device array that
+// every GPU the library runs on holds until the process ends.  Host code never uses
+// the array's name as an address: the address of each device's copy is resolved
+// once, with that device current, and kept per device.
+constexpr int64_t kScratchBytes = (int64_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// The current device's scratch address, or a negative status.
+int current_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KDA_ERR_HIP;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return KDA_ERR_HIP;
+  *ptr = g_scratch_ptr[dev];
+  return KDA_OK;
 }
 
 // Validates, fills the launch parameters and enqueues the kernel, or with a
@@ -351,6 +377,35 @@ int kda_fwd_split(const void* q, const void* k, const void* v, const void* g, co
                 H, D, stream, chunk_size, v_tile, nullptr, 0, true, workspace, workspace_bytes);
 }
 
+int kda_fwd_split_noalloc(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, float scale, void* out, const float* A_log,
+                          const float* dt_bias, float lower_bound, const void* initial_state,
+                          int initial_state_dtype, void* final_state, int final_state_dtype,
+                          const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T,
+                          int64_t H, int64_t D, void* stream, int chunk_size, int v_tile) {
+  // the arguments first (nothing touches the device on a validation error), then
+  // the workspace size against the scratch array's
+  int chunk = 0, vt = 0;
+  const int st = resolve(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                         initial_state, initial_state_dtype, final_state, final_state_dtype,
+                         cu_seqlens, num_seqs, B, T, H, D, chunk_size, v_tile, nullptr, &chunk,
+                         &vt);
+  if (st != KDA_OK) return st;
+  if (!kda::kda_split_supported(static_cast<int>(D), tile_rows(chunk), vt))
+    return KDA_ERR_BAD_SCHEDULE;
+  const int64_t head_bytes = split_head_bytes(B * T, num_seqs, H, D, chunk);
+  if (head_bytes < 0) return static_cast<int>(head_bytes);
+  if (head_bytes > kScratchBytes / H) return KDA_ERR_SCRATCH_TOO_SMALL;
+  void* ws = nullptr;
+  const int sp = current_scratch(&ws);
+  if (sp != KDA_OK) return sp;
+  return launch(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T,
+                H, D, stream, chunk_size, v_tile, nullptr, 0, true, ws, kScratchBytes);
+}
+
+int64_t kda_split_noalloc_max_bytes(void) { return kScratchBytes; }
+
 float kda_chunk_anchor(float lower_bound, int chunk_size) {
   const double span = chunk_span(lower_bound, chunk_size);
   // one-token chunks past the window floor the decay at the window's width
@@ -373,6 +428,9 @@ const char* kda_status_string(int status) {
     case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported an error";
     case KDA_ERR_BAD_WORKSPACE:
       return "KDA_ERR_BAD_WORKSPACE: the workspace is smaller than kda_split_workspace_bytes";
+    case KDA_ERR_SCRATCH_TOO_SMALL:
+      return "KDA_ERR_SCRATCH_TOO_SMALL: kda_split_workspace_bytes of this call exceeds the "
+             "64 MiB scratch of kda_fwd_split_noalloc (use kda_fwd_split with a workspace)";
     default: return "KDA_ERR_UNKNOWN";
   }
 }

@@ -29,7 +29,8 @@
  *   - Kernels launch on the calling thread's current HIP device: the pointers
  *     and `stream` must belong to it (hipSetDevice before the call).
  *   - The library allocates nothing and keeps no global state; calls on
- *     different streams may run concurrently.
+ *     different streams may run concurrently.  The one exception is
+ *     kda_fwd_split_noalloc, whose scratch is a static device array per GPU.
  *   - kda_fwd is asynchronous: it validates on the host, enqueues one kernel on
  *     `stream` and returns.  It never reads device memory on the host (in
  *     particular not cu_seqlens) and never synchronises.
@@ -67,6 +68,8 @@ extern "C" {
 #define KDA_ERR_BAD_SCHEDULE (-8)    /* unsupported forced chunk size or value tile      */
 #define KDA_ERR_HIP (-9)             /* the HIP runtime reported an error at launch      */
 #define KDA_ERR_BAD_WORKSPACE (-10)  /* kda_fwd_split: workspace smaller than required   */
+#define KDA_ERR_SCRATCH_TOO_SMALL (-11) /* kda_fwd_split_noalloc: the call's workspace   */
+                                        /* exceeds kda_split_noalloc_max_bytes()         */
 
 /* State dtype codes (initial_state_dtype, final_state_dtype). */
 #define KDA_DTYPE_BF16 0
@@ -233,6 +236,36 @@ int kda_fwd_split(const void* q, const void* k, const void* v, const void* g, co
                   void* final_state, int final_state_dtype, const int64_t* cu_seqlens,
                   int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t D, void* stream,
                   void* workspace, int64_t workspace_bytes, int chunk_size, int v_tile);
+
+/*
+ * kda_fwd_split_noalloc -- kda_fwd_split for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The workspace is the library's own scratch: a static device
+ * array of kda_split_noalloc_max_bytes() bytes (64 MiB) that each GPU the library
+ * runs on holds until the process ends.  Its address is resolved once per device,
+ * on the first call with that device current; the call allocates nothing.
+ *   chunk_size, v_tile  as for kda_fwd_split.
+ * A call whose kda_split_workspace_bytes(B * T, num_seqs, H, D, lower_bound,
+ * chunk_size) exceeds the scratch returns KDA_ERR_SCRATCH_TOO_SMALL before
+ * anything is enqueued (for example 96 heads hold 20 records of 33,280 bytes each:
+ * T_total + 32 num_seqs below about 608 tokens at 32-token chunks).  Every call on a
+ * GPU shares that GPU's array and leaves its records there; calls that overlap in
+ * time on one GPU (concurrent streams, or threads) race on it and must be
+ * serialised by the caller.  Nothing in the array needs to start at zero: every
+ * record is written by the call's prep kernel before its recurrent kernel reads it.
+ * The results are bitwise those of kda_fwd_split.  Returns KDA_OK, a kda_fwd_split
+ * status, KDA_ERR_SCRATCH_TOO_SMALL, or KDA_ERR_HIP if the scratch address cannot
+ * be resolved.
+ */
+int kda_fwd_split_noalloc(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, float scale, void* out, const float* A_log,
+                          const float* dt_bias, float lower_bound, const void* initial_state,
+                          int initial_state_dtype, void* final_state, int final_state_dtype,
+                          const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T,
+                          int64_t H, int64_t D, void* stream, int chunk_size, int v_tile);
+
+/* kda_split_noalloc_max_bytes -- bytes of kda_fwd_split_noalloc's scratch (64 MiB). */
+int64_t kda_split_noalloc_max_bytes(void);
 
 /*
  * kda_longest_first -- writes the longest-first order of a packed batch for

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, -11, -1):
+    for code in range(0, -12, -1):
         s = kda.kda_status_string(code)
         assert s.startswith("KDA_")
     assert "UNKNOWN" in kda.kda_status_string(-1234)
@@ -337,3 +337,20 @@ def test_split_slot_numbering_is_injective_and_fits():
                     seen.add(j)
                     # the binary search's answer: the last sequence whose first slot <= j
                     assert max(m for m in range(len(lens)) if firsts[m] <= j) == n
+
+
+def test_noalloc_split_rejects_workspaces_beyond_its_scratch(lib):
+    """kda_fwd_split_noalloc checks the call's workspace against its 64 MiB static
+    scratch on the host and returns before touching the device."""
+    cap = lib.kda_split_noalloc_max_bytes()
+    assert cap == 64 << 20
+    noalloc = lib.kda_fwd_split_noalloc
+    # 96 heads of 2 x 1024 tokens need 96 * 67 records of 33,280 bytes: too many
+    a = _args(B=2, T=1024, H=96)
+    assert kda.kda_split_workspace_bytes(2048, 2, 96, 128, -5.0) > cap
+    assert noalloc(*a[:-2], None, 0, 0) == kda.KDA_ERR_SCRATCH_TOO_SMALL
+    # validation errors come first, exactly as for kda_fwd_split
+    assert noalloc(*_args(B=2, T=1024, H=96, lb=1.0)[:-2], None, 0, 0) == \
+        kda.KDA_ERR_BAD_LOWER_BOUND
+    assert noalloc(*_args(D=64)[:-2], None, 0, 0) == kda.KDA_ERR_BAD_SCHEDULE
+    assert noalloc(*a[:-2], None, 24, 0) == kda.KDA_ERR_BAD_SCHEDULE
