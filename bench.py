@@ -105,6 +105,9 @@ def cpu_baseline(inp, min_wall: float):
     import torch
 
     import oracle
+    if oracle.override_active():
+        raise RuntimeError("KDA_ORACLE_LIB_OVERRIDE is set: the CPU baseline would time a "
+                           "swapped oracle")
     B, T, H, D = inp["q"].shape
     oracle._load()
     # widen to fp64 outside the timed region, exactly as the oracle would

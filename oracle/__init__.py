@@ -34,6 +34,11 @@ _LIB_OVERRIDE = os.environ.get("KDA_ORACLE_LIB_OVERRIDE")
 _lib = None
 
 
+def override_active() -> bool:
+    """Whether KDA_ORACLE_LIB_OVERRIDE (the mutation test's swapped build) is in force."""
+    return bool(_LIB_OVERRIDE)
+
+
 def build(force: bool = True) -> str:
     """Compile ``kda_oracle.c`` into ``libkda_oracle.so`` with gcc (fp64, -O2, OpenMP)."""
     if force or not os.path.exists(_LIB_PATH):

@@ -1,9 +1,9 @@
-"""Study (CPU, not a test): where the GPU kernel's error against the oracle comes from.
+"""Error budget of the GPU kernel (CPU): where its error against the oracle comes from.
 
 The kernel computes the chunk form of the FlashInfer PR #4262 summary (section 2's
 centred operands, section 3's decomposition) with bf16 matrix-core operands and fp32
-accumulation.  This script follows the same steps in fp64 and rounds to bf16 (round
-to nearest even) at each site where the kernel does, one switch per site:
+accumulation.  ``emulate`` follows the same steps in fp64 and rounds to bf16 (round to
+nearest even) at each site where the kernel does, one switch per site:
 
   qc, kc, ki, kr   the centred operands Qc, Kc, Ki and the decayed Kr
   mqk    the stored Mqk (as 2^-Ca Mqk; the power of two is exact)
@@ -13,10 +13,10 @@ to nearest even) at each site where the kernel does, one switch per site:
   u      U_top inside the solve, and U for the state update and the output
   out    the output tile
 
-It runs on seeded inputs of the library's input recipe and prints the relative L2
-error of ``out`` and of the fp32 final state against the fp64 oracle: with every site
-rounded (about what the GPU measures), and with each site left unrounded in turn.
-Usage: ``python tests/study_error_budget.py``.
+The tests hold the relative L2 errors of ``out`` against the fp64 oracle to the values the
+design notes quote (every site rounded, which is what the GPU measures; each site alone),
+within the slack stated in each test.  ``python tests/test_error_budget.py`` prints the
+full table.
 """
 from __future__ import annotations
 
@@ -99,17 +99,61 @@ def _rel(x, ref):
     return float(np.linalg.norm(x - ref) / np.linalg.norm(ref))
 
 
+CASES = {"D=128, lb=-5": dict(D=128, lower_bound=-5.0),
+         "D=128, lb=-0.01": dict(D=128, lower_bound=-0.01),
+         "D=32, lb=-0.01": dict(D=32, lower_bound=-0.01)}
+
+
+def _case(name):
+    w = Workload("budget", B=1, T=512, H=2, seed=41, state_in="fp32", state_out="fp32",
+                 **CASES[name])
+    inp = make_inputs(w, device="cpu")
+    o_ref, f_ref = oracle.kda_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                  inp["scale"], inp["A_log"], inp["dt_bias"],
+                                  inp["lower_bound"], inp["initial_state"])
+    return inp, o_ref[0], f_ref[0]
+
+
+# out rel-L2 with every site rounded (the GPU measures 3.98e-3, 4.29e-3 and 4.70e-3 on the
+# same shapes), and with one site rounded alone at D = 128, lb = -5
+ALL_SITES = {"D=128, lb=-5": 3.99e-3, "D=128, lb=-0.01": 4.29e-3, "D=32, lb=-0.01": 4.69e-3}
+ONE_SITE = {"qc": 1.75e-3, "kc": 1.6e-5, "ki": 1.70e-3, "kr": 4.5e-5, "mqk": 1.64e-3,
+            "sol": 1.8e-5, "scopy": 6.7e-5, "r": 1.67e-3, "u": 1.66e-3, "out": 1.67e-3}
+
+
+def test_every_site_rounded_reproduces_the_measured_errors():
+    """Within 3% of the quoted values, and below the 5e-3 bound with 5% to spare."""
+    for name, want in ALL_SITES.items():
+        inp, o_ref, _ = _case(name)
+        o, _ = emulate(inp, set(SITES))
+        got = _rel(o, o_ref)
+        assert abs(got - want) <= 0.03 * want, (name, got, want)
+        assert got <= 0.95 * 5e-3, (name, got)
+
+
+def test_single_sites_and_their_quadrature_sum():
+    """Each site alone within 10% of the quoted value; the six sites of about one bf16
+    rounding each (1.6e-3 to 1.8e-3) add up in quadrature to the every-site error within
+    10%; and the site the design notes name as the cheapest to split (Mqk in two bf16
+    parts, which removes its rounding) lowers the strong-decay error to 3.69e-3."""
+    inp, o_ref, _ = _case("D=128, lb=-5")
+    alone = {}
+    for site, want in ONE_SITE.items():
+        o, _ = emulate(inp, {site})
+        alone[site] = _rel(o, o_ref)
+        assert abs(alone[site] - want) <= 0.10 * want, (site, alone[site], want)
+    big = [v for v in alone.values() if v > 1e-3]
+    assert len(big) == 6
+    o, _ = emulate(inp, set(SITES))
+    total = _rel(o, o_ref)
+    assert abs(math.sqrt(sum(v * v for v in alone.values())) - total) <= 0.10 * total
+    o, _ = emulate(inp, set(SITES) - {"mqk"})
+    assert abs(_rel(o, o_ref) - 3.69e-3) <= 0.03 * 3.69e-3
+
+
 def main():
-    cases = [("D=128, lb=-5", dict(D=128, lower_bound=-5.0)),
-             ("D=128, lb=-0.01", dict(D=128, lower_bound=-0.01)),
-             ("D=32, lb=-0.01", dict(D=32, lower_bound=-0.01))]
-    for name, kw in cases:
-        w = Workload("budget", B=1, T=512, H=2, seed=41, state_in="fp32", state_out="fp32", **kw)
-        inp = make_inputs(w, device="cpu")
-        o_ref, f_ref = oracle.kda_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
-                                      inp["scale"], inp["A_log"], inp["dt_bias"],
-                                      inp["lower_bound"], inp["initial_state"])
-        o_ref, f_ref = o_ref[0], f_ref[0]
+    for name in CASES:
+        inp, o_ref, f_ref = _case(name)
         print("== %s (T = 512, H = 2)" % name)
         o, f = emulate(inp, set(SITES))
         print("  every site rounded:   out %.2e  state %.2e" % (_rel(o, o_ref), _rel(f, f_ref)))

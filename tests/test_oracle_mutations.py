@@ -73,3 +73,18 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, "planted mistake %r passed every pin:\n%s" % (name, r.stdout[-2000:])
+
+
+def test_override_refuses_gpu_sessions(tmp_path):
+    """With the override set, a session that collects a GPU test fails at collection
+    (so no GPU parity run can compare against a planted mistake), while a CPU-only
+    session (the pin suite above) runs."""
+    env = dict(os.environ, KDA_ORACLE_LIB_OVERRIDE=str(tmp_path / "none.so"))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "--collect-only", "-m", "gpu",
+                        "-p", "no:cacheprovider", os.path.join(ROOT, "tests", "test_gpu_sweep.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0 and "KDA_ORACLE_LIB_OVERRIDE" in (r.stdout + r.stderr)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "--collect-only",
+                        "-p", "no:cacheprovider", os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout[-1000:]
