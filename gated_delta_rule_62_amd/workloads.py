@@ -10,11 +10,14 @@ workloads the library is measured and checked on (head dim 128 unless stated):
   varlen3   B=1 packed lengths [300, 700, 1024], H=96, fp32 state in and out
   long      B=1, T=32768, H=96, zero initial state
   many      64 packed sequences, lengths uniform in [1, 512], H=32, bf16 state
+            (the lengths from a CPU generator seeded 5, so every device draws the same
+            batch: T_total 15,579, longest 496, shortest 6)
 
 q, k, v, g and beta are N(0, 1) drawn in fp32 and rounded to bf16 (round to
 nearest even); A_log ~ U(0, 1) [H]; dt_bias ~ U(0, 1) [H, D]; lower_bound = -5;
 scale = 1/sqrt(D).  The draw order is: lengths, q, k, v, g, beta, A_log,
-dt_bias, initial state.  The generator is torch's, seeded per workload, on the
+dt_bias, initial state.  Random lengths come from torch's CPU generator seeded
+``length_seed``; the tensors from torch's generator seeded per workload on the
 device requested (a CPU draw and a GPU draw of the same seed differ; each run
 hands the same tensors to both sides).
 """
@@ -38,6 +41,7 @@ class Workload:
     lengths: Optional[list] = None          # varlen sequence lengths (B == 1)
     n_random_seqs: int = 0                  # draw this many lengths in [1, max_len]
     max_len: int = 0
+    length_seed: int = 0                    # CPU generator seed of the random lengths
     state_in: Optional[str] = "bf16"        # None | "zero_bf16" | "bf16" | "fp32"
     state_out: str = "bf16"                 # "bf16" | "fp32"
     lower_bound: float = -5.0
@@ -53,7 +57,7 @@ WORKLOADS = {
                         state_in="fp32", state_out="fp32"),
     "long": Workload("long", B=1, T=32768, H=96, D=128, seed=3, state_in="zero_bf16"),
     "many": Workload("many", B=1, T=0, H=32, D=128, seed=4, n_random_seqs=64, max_len=512,
-                     state_in="bf16"),
+                     length_seed=5, state_in="bf16"),
 }
 
 
@@ -74,8 +78,8 @@ def make_inputs(w: Workload, device="cpu", seed: Optional[int] = None) -> dict:
     if w.lengths is not None:
         lengths = list(w.lengths)
     elif w.n_random_seqs:
-        lengths = torch.randint(1, w.max_len + 1, (w.n_random_seqs,), generator=gen,
-                                device=device).tolist()
+        lengths = torch.randint(1, w.max_len + 1, (w.n_random_seqs,),
+                                generator=torch.Generator().manual_seed(w.length_seed)).tolist()
     if lengths is not None:
         B, T = 1, int(sum(lengths))
         N = len(lengths)
