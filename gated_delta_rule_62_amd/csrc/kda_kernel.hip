@@ -251,7 +251,8 @@ struct alignas(16) Slot : QcKc<F, F::SO> {
   u16 Kr[F::C][F::LDR];      // columns in state-row order (read transposed)
   u16 SOL[F::C][F::LDC];     // X11 2^-16, X22 2^-16 (X = (I + L)^-1 diagonal blocks) and
                              // -L21 2^16: the solve then yields U 2^-16
-  u16 Mqk[F::C][F::LDC];
+  u16 Mqk[F::C][F::LDC];      // 2^-Ca Mqk in two bf16 parts: Mqk, the nearest bf16, and
+  u16 MqkLo[F::C][F::LDC];    // MqkLo, the nearest bf16 to the remainder
   u16 V[F::C][F::LDV];
   float a[2 * F::D];         // 2^G_T in state-row order (second half: discarded writes)
   float beta[F::C];          // sigmoid(beta), zero past the sequence
@@ -681,6 +682,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     for (int i = tid; i < kSlots * 16 * 16; i += F::NTHR) {
       const int b = i >> 8, r = (i >> 4) & 15, c = 16 + (i & 15);
       sm.slot[b].Mqk[r][c] = 0;
+      sm.slot[b].MqkLo[r][c] = 0;
     }
   }
 
@@ -762,18 +764,24 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       }
     }
     // O = 2^Ca (O0' + U Mqk'^T), Mqk' = 2^-Ca Mqk: U as the A operand (value rows),
-    // Mqk' rows as B (token columns).  Before the state update, so that O's
-    // accumulators are free while the update's operands are read.
+    // Mqk' rows as B (token columns), Mqk' in its two bf16 parts (one product each).
+    // Before the state update, so that O's accumulators are free while the update's
+    // operands are read.
     const __amdgpu_buffer_rsrc_t ro =
         make_rsrc(p.out + (ck.tok * H + ck.h) * D + vt_idx * VT, ck.valid * (int)row_bytes);
 #pragma unroll
     for (int ct = 0; ct < F::CT; ++ct) {
-      u32x4_t bM;
-      if constexpr (F::CT == 2) bM = lds_op_cc(&cur.Mqk[16 * ct + l16][0], lg);
-      else bM = lds_op_pad(&cur.Mqk[l16][0], lg);
+      u32x4_t bM, bML;
+      if constexpr (F::CT == 2) {
+        bM = lds_op_cc(&cur.Mqk[16 * ct + l16][0], lg);
+        bML = lds_op_cc(&cur.MqkLo[16 * ct + l16][0], lg);
+      } else {
+        bM = lds_op_pad(&cur.Mqk[l16][0], lg);
+        bML = lds_op_pad(&cur.MqkLo[l16][0], lg);
+      }
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) {
-        const f32x4_t o = c1o * mfma_k32(bU[nt], bM, O[ct][nt]);
+        const f32x4_t o = c1o * mfma_k32(bU[nt], bML, mfma_k32(bU[nt], bM, O[ct][nt]));
         // lane: token 16 ct + l16, values wv0 + 16 nt + 4 lg .. +3
         const u32x2_t w = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
         __builtin_amdgcn_raw_buffer_store_b64(
@@ -1056,7 +1064,10 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int i = 16 * ti + 4 * lg + ii;
-        cur.Mqk[i][j] = to_bf16((j <= i) ? acc[ii] * c1i : 0.f);  // stored as 2^-Ca Mqk
+        const float m = (j <= i) ? acc[ii] * c1i : 0.f;  // stored as 2^-Ca Mqk, in two parts
+        const u16 hi = to_bf16(m);
+        cur.Mqk[i][j] = hi;
+        cur.MqkLo[i][j] = to_bf16(m - bf2f(hi));
       }
       return;
     }
@@ -1135,14 +1146,14 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
 
   // ======================= split: prepared-chunk records ======================
   // A record is the byte image of what the state side reads from LDS for one
-  // chunk: Qc, Kc (shared tiles), then Kr, SOL, Mqk and a of its slot, in 16-byte
+  // chunk: Qc, Kc, then Kr, SOL, Mqk (two parts) and a of its slot, in 16-byte
   // units.  The prep kernel stores it, the recurrent kernel's job waves load it one
   // chunk ahead (as q and k are loaded in the fused kernel) and copy it into LDS.
   constexpr int kQU = F::C * F::LDQ * 2 / 16;
   constexpr int kRU = F::C * F::LDR * 2 / 16;
   constexpr int kCU = F::C * F::LDC * 2 / 16;
   constexpr int kAU = F::D * 4 / 16;
-  constexpr int kRecUnits = 2 * kQU + kRU + 2 * kCU + kAU;
+  constexpr int kRecUnits = 2 * kQU + kRU + 3 * kCU + kAU;
   static_assert(kRecUnits * 16 == kda_record_bytes(D, C), "record layout");
   constexpr int kRecPerJob = (kRecUnits + F::NJW * 64 - 1) / (F::NJW * 64);
   auto rec_lds = [&](Slot<F>& sl, int u) -> u32x4_t* {
@@ -1157,9 +1168,12 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     } else if (u < 2 * kQU + kRU + 2 * kCU) {
       b = reinterpret_cast<char*>(&sl.Mqk[0][0]);
       o = u - 2 * kQU - kRU - kCU;
+    } else if (u < 2 * kQU + kRU + 3 * kCU) {
+      b = reinterpret_cast<char*>(&sl.MqkLo[0][0]);
+      o = u - 2 * kQU - kRU - 2 * kCU;
     } else {
       b = reinterpret_cast<char*>(&sl.a[0]);
-      o = u - 2 * kQU - kRU - 2 * kCU;
+      o = u - 2 * kQU - kRU - 3 * kCU;
     }
     return reinterpret_cast<u32x4_t*>(b + 16 * o);
   };

@@ -45,10 +45,10 @@ struct KdaParams {
 
 // Bytes of one prepared-chunk record for head dimension D and tile height C: the
 // byte images of the centred operands Qc and Kc ([C][D+16] bf16 each), the decayed
-// keys Kr ([C][D+16] bf16), the solve operands and Mqk ([C][C+8] bf16 each) and the
-// chunk decay a (D fp32), as the recurrent side reads them from LDS.
+// keys Kr ([C][D+16] bf16), the solve operands and Mqk in two parts ([C][C+8] bf16
+// each) and the chunk decay a (D fp32), as the recurrent side reads them from LDS.
 constexpr int64_t kda_record_bytes(int64_t D, int64_t C) {
-  return 2 * C * (D + 16) * 2 + C * (D + 16) * 2 + 2 * C * (C + 8) * 2 + D * 4;
+  return 2 * C * (D + 16) * 2 + C * (D + 16) * 2 + 3 * C * (C + 8) * 2 + D * 4;
 }
 
 // Slots per head of a split workspace: chunk starts never share a slot, and none

@@ -198,7 +198,7 @@ int kda_fwd_transposed_state(const void* q, const void* k, const void* v, const 
  *               kda_fwd_split the same chunk_size.
  * One record per slot and head: the prepared operands of one chunk (Qc, Kc, Kr,
  * the solve operands, Mqk and the decay, in the layout the recurrent kernel copies
- * into LDS; 33,280 bytes at 32-token chunks).  A head has floor(T_total / chunk)
+ * into LDS; 35,840 bytes at 32-token chunks).  A head has floor(T_total / chunk)
  * + num_seqs + 1 slots.  Returns the size, or a negative status
  * (KDA_ERR_BAD_SHAPE, also when a head's records reach 2^31 bytes or the prep
  * kernel's grid of slots times heads workgroups of 512 threads exceeds 2^32 - 1
@@ -247,8 +247,8 @@ int kda_fwd_split(const void* q, const void* k, const void* v, const void* g, co
  *   chunk_size, v_tile  as for kda_fwd_split.
  * A call whose kda_split_workspace_bytes(B * T, num_seqs, H, D, lower_bound,
  * chunk_size) exceeds the scratch returns KDA_ERR_SCRATCH_TOO_SMALL before
- * anything is enqueued (for example 96 heads hold 20 records of 33,280 bytes each:
- * T_total + 32 num_seqs below about 608 tokens at 32-token chunks).  Every call on a
+ * anything is enqueued (for example 96 heads hold 19 records of 35,840 bytes each:
+ * T_total + 32 num_seqs below about 576 tokens at 32-token chunks).  Every call on a
  * GPU shares that GPU's array and leaves its records there; calls that overlap in
  * time on one GPU (concurrent streams, or threads) race on it and must be
  * serialised by the caller.  Nothing in the array needs to start at zero: every

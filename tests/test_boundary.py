@@ -226,11 +226,11 @@ def test_ordered_and_longest_first_validation(lib):
 
 def test_split_workspace_bytes(lib):
     """One record per slot and head: the byte images of Qc, Kc ([C][D+16] bf16), Kr
-    ([C][D+16] bf16), the solve operands and Mqk ([C][C+8] bf16) and the decay (D fp32);
-    floor(T_total / chunk) + num_seqs + 1 slots per head."""
-    rec32 = 2 * 32 * 144 * 2 + 32 * 144 * 2 + 2 * 32 * 40 * 2 + 128 * 4
-    rec16 = 2 * 16 * 144 * 2 + 16 * 144 * 2 + 2 * 16 * 24 * 2 + 128 * 4
-    assert rec32 == 33280 and rec16 == 15872
+    ([C][D+16] bf16), the solve operands and Mqk in two parts ([C][C+8] bf16) and the
+    decay (D fp32); floor(T_total / chunk) + num_seqs + 1 slots per head."""
+    rec32 = 2 * 32 * 144 * 2 + 32 * 144 * 2 + 3 * 32 * 40 * 2 + 128 * 4
+    rec16 = 2 * 16 * 144 * 2 + 16 * 144 * 2 + 3 * 16 * 24 * 2 + 128 * 4
+    assert rec32 == 35840 and rec16 == 16640
     ws = kda.kda_split_workspace_bytes
     assert ws(32768, 1, 96, 128, -5.0) == 96 * (1024 + 2) * rec32
     assert ws(2024, 3, 96, 128, -5.0) == 96 * (63 + 4) * rec32
