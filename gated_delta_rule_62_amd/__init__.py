@@ -14,6 +14,7 @@ import os
 from ._build import LIB_PATH, build  # noqa: F401  (build() is the in-tree compile step)
 
 __all__ = ["kda_fwd", "kda_fwd_sched", "kda_fwd_ordered", "kda_fwd_transposed_state",
+           "kda_fwd_bf16_state",
            "kda_fwd_split", "kda_split_workspace_bytes", "kda_fwd_split_noalloc",
            "kda_longest_first", "kda_fwd_check", "c_args",
            "kda_chunk_anchor", "kda_status_string", "KdaError", "library_path", "load_library"]
@@ -68,6 +69,8 @@ def load_library():
     lib.kda_fwd_ordered.restype = i32
     lib.kda_fwd_transposed_state.argtypes = common + [vp]
     lib.kda_fwd_transposed_state.restype = i32
+    lib.kda_fwd_bf16_state.argtypes = common + [vp, i32, i32]
+    lib.kda_fwd_bf16_state.restype = i32
     lib.kda_longest_first.argtypes = [vp, i64, vp, vp]
     lib.kda_longest_first.restype = i32
     lib.kda_split_workspace_bytes.argtypes = [i64, i64, i64, i64, f32, i32]
@@ -213,6 +216,19 @@ def kda_fwd_transposed_state(q, k, v, g, beta, scale, out, A_log, dt_bias, lower
                   final_state, cu_seqlens, stream)
     with _on_device(q):
         st = load_library().kda_fwd_transposed_state(*args)
+    if st != KDA_OK:
+        raise KdaError(st)
+
+
+def kda_fwd_bf16_state(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                       initial_state=None, final_state=None, cu_seqlens=None,
+                       chunk_size: int = 0, v_tile: int = 0, stream=None) -> None:
+    """``kda_fwd_sched`` with the recurrent state kept in bf16 in LDS (widened to fp32
+    for each chunk's update, rounded once back).  D = 128 with 32-token chunks only."""
+    args = c_args(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                  final_state, cu_seqlens, stream)
+    with _on_device(q):
+        st = load_library().kda_fwd_bf16_state(*args, int(chunk_size), int(v_tile))
     if st != KDA_OK:
         raise KdaError(st)
 

@@ -204,13 +204,15 @@ int launch(const void* q, const void* k, const void* v, const void* g, const voi
            int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B,
            int64_t T, int64_t H, int64_t D, void* stream, int chunk_size, int v_tile,
            const int32_t* seq_order, int state_kv, bool split = false, void* workspace = nullptr,
-           int64_t workspace_bytes = 0) {
+           int64_t workspace_bytes = 0, bool lds_state = false) {
   int chunk = 0, vt = 0;
   const int st = resolve(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
                          initial_state, initial_state_dtype, final_state, final_state_dtype,
                          cu_seqlens, num_seqs, B, T, H, D, chunk_size, v_tile, seq_order, &chunk,
                          &vt);
   if (st != KDA_OK) return st;
+  if (lds_state && !kda::kda_slds_supported(static_cast<int>(D), tile_rows(chunk), vt))
+    return KDA_ERR_BAD_SCHEDULE;
   int64_t head_bytes = 0;
   if (split) {
     if (!kda::kda_split_supported(static_cast<int>(D), tile_rows(chunk), vt))
@@ -273,11 +275,11 @@ int launch(const void* q, const void* k, const void* v, const void* g, const voi
   p.anchor = kda_chunk_anchor(lower_bound, chunk);
   p.ws = workspace;
   p.ws_head_bytes = head_bytes;
-  const hipError_t e =
-      split ? kda::launch_kda_split(p, static_cast<int>(D), tile_rows(chunk), vt,
-                                    static_cast<hipStream_t>(stream))
-            : kda::launch_kda_fwd(p, static_cast<int>(D), tile_rows(chunk), vt,
-                                  static_cast<hipStream_t>(stream));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int d = static_cast<int>(D), c = tile_rows(chunk);
+  const hipError_t e = split       ? kda::launch_kda_split(p, d, c, vt, hs)
+                       : lds_state ? kda::launch_kda_fwd_slds(p, d, c, vt, hs)
+                                   : kda::launch_kda_fwd(p, d, c, vt, hs);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -306,6 +308,17 @@ int kda_fwd_sched(const void* q, const void* k, const void* v, const void* g, co
   return launch(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                 initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T,
                 H, D, stream, chunk_size, v_tile, nullptr, 0);
+}
+
+int kda_fwd_bf16_state(const void* q, const void* k, const void* v, const void* g,
+                       const void* beta, float scale, void* out, const float* A_log,
+                       const float* dt_bias, float lower_bound, const void* initial_state,
+                       int initial_state_dtype, void* final_state, int final_state_dtype,
+                       const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T,
+                       int64_t H, int64_t D, void* stream, int chunk_size, int v_tile) {
+  return launch(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T,
+                H, D, stream, chunk_size, v_tile, nullptr, 0, false, nullptr, 0, true);
 }
 
 int kda_fwd_ordered(const void* q, const void* k, const void* v, const void* g,

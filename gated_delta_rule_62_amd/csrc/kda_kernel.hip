@@ -258,8 +258,18 @@ struct alignas(16) Slot : QcKc<F, F::SO> {
   float beta[F::C];          // sigmoid(beta), zero past the sequence
 };
 
-template <class F, int NSLOT>
-struct alignas(16) Smem : QcKc<F, !F::SO> {  // (Qc, Kc: the chunk whose state side,
+// The bf16 state of the LDS-state mode: rows are the workgroup's value rows, keys
+// contiguous (the [V, K] layout of the state tensors), padded by 16 keys so that
+// 16-byte reads of 16 rows fall in distinct banks.
+template <class F, bool kHere>
+struct StateLds {};
+template <class F>
+struct alignas(16) StateLds<F, true> {
+  u16 Sb[F::VT][F::D + 16];
+};
+
+template <class F, int NSLOT, bool kSlds = false>
+struct alignas(16) Smem : QcKc<F, !F::SO>, StateLds<F, kSlds> {  // (Qc, Kc: the chunk whose state side,
                              // matrices and preparation alternate in them)
   Slot<F> slot[NSLOT];       // two alternate in the chunk loop; the prep kernel uses one
   u16 Ki[F::C][F::LDQ];
@@ -414,12 +424,19 @@ __device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off,
 constexpr int kModeFused = 0;
 constexpr int kModePrep = 1;
 constexpr int kModeRecur = 2;
+// The fused forward with the state kept in LDS as bf16 between chunks and updated
+// with fp32 arithmetic (FlashKDA's on-chip bf16 state, as "How FlashKDA Stores
+// On-Chip Recurrent State in BF16 for Memory Efficiency" describes it): one
+// rounding per chunk, state-only schedule only.
+constexpr int kModeSlds = 3;
 
 template <int D, int C, int VT, int NW, int NSW, int MODE>
 __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   using F = Cfg<D, C, VT, NW, NSW>;
   static_assert(MODE == kModeFused || F::SPLIT, "the split runs the role-split schedules only");
-  __shared__ Smem<F, MODE == kModePrep ? 1 : 2> sm;
+  constexpr bool SLDS = MODE == kModeSlds;
+  static_assert(!SLDS || F::SO, "the LDS state runs the state-only schedule only");
+  __shared__ Smem<F, MODE == kModePrep ? 1 : 2, SLDS> sm;
   // The centred operands of the chunk prepared in slot sl.
   auto qc_of = [&](Slot<F>& sl) -> u16(*)[F::LDQ] {
     if constexpr (F::SO) return sl.Qc;
@@ -552,6 +569,9 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   const int wv0 = wave * 16 * F::NTW;          // first value column of a state wave (in the tile)
   const int vbase = vt_idx * VT + wv0;         // ... in the head
   f32x4_t S[F::KT][F::NTW];
+  // LDS-state mode: the chunk's decay in state-row order, read in phase A (in phase B
+  // the gate waves overwrite the slot's decay vector with that of two chunks ahead)
+  f32x4_t Adec[F::KT];
   // State I/O goes through a buffer descriptor based at the (sequence, head) state,
   // with one lane offset and a per-tile constant in the instruction's scalar offset
   // (no 64-bit address per tile).
@@ -676,6 +696,74 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       }
   };
 
+  // LDS-state mode: the state waves copy their value rows of the initial state into
+  // the bf16 LDS state (rounded, and 2^16 below scale like the accumulators of the
+  // register state) and back out at the end; eight keys per lane and access.
+  constexpr int kSRowUnits = D / 8;                 // 8-key units per state row
+  constexpr int kSUnits = 16 * F::NTW * kSRowUnits;  // units of a state wave's rows
+  static_assert(kSUnits % 64 == 0, "state row units per lane");
+  auto slds_in = [&](int64_t sbase) __attribute__((always_inline)) {
+    if constexpr (SLDS) {
+      const int es = p.s_in_fp32 ? 4 : 2;
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(static_cast<const char*>(p.s_in) + sbase * es, D * D * es);
+#pragma unroll
+      for (int i = 0; i < kSUnits / 64; ++i) {
+        const int u = lane + 64 * i;
+        const int r = u / kSRowUnits, k0 = 8 * (u % kSRowUnits);
+        const uint32_t off = (uint32_t)(((vbase + r) * D + k0) * es);
+        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (p.s_in != nullptr) {
+          if (p.s_in_fp32) {
+            const f32x4_t a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+            const f32x4_t b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+          } else {
+            const u32x4_t w = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { x[2 * e] = bflo(w[e]); x[2 * e + 1] = bfhi(w[e]); }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= kStateDown;
+        store_bf16<8>(&sm.Sb[wv0 + r][k0], x);
+      }
+    }
+  };
+  auto slds_out = [&](int64_t sbase) __attribute__((always_inline)) {
+    if constexpr (SLDS) {
+      if (p.s_out == nullptr) return;
+      const int es = p.s_out_fp32 ? 4 : 2;
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(static_cast<char*>(p.s_out) + sbase * es, D * D * es);
+#pragma unroll
+      for (int i = 0; i < kSUnits / 64; ++i) {
+        const int u = lane + 64 * i;
+        const int r = u / kSRowUnits, k0 = 8 * (u % kSRowUnits);
+        const uint32_t off = (uint32_t)(((vbase + r) * D + k0) * es);
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(&sm.Sb[wv0 + r][k0]);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = kStateUp * bflo(w[e]);
+          x[2 * e + 1] = kStateUp * bfhi(w[e]);
+        }
+        if (p.s_out_fp32) {
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(u32x4_t, f32x4_t{x[0], x[1], x[2], x[3]}), rs, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(u32x4_t, f32x4_t{x[4], x[5], x[6], x[7]}), rs, off + 16, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(
+              u32x4_t{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]),
+                      pack_bf16(x[6], x[7])},
+              rs, off, 0, 0);
+        }
+      }
+    }
+  };
+
   // The block above the diagonal of Mqk is never written: zero it once.
   if constexpr (F::CT == 2) {
     constexpr int kSlots = MODE == kModePrep ? 1 : 2;
@@ -698,15 +786,24 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
 #pragma unroll
     for (int ks = 0; ks < F::KS; ++ks) {
       u32x4_t bS[F::NTW];
+      if constexpr (SLDS) {
+        // the bf16 state is the operand: keys 32 ks + 8 lg .. + 7 of value row l16
 #pragma unroll
-      for (int nt = 0; nt < F::NTW; ++nt)
-        bS[nt] = acc_pair_to_op(S[2 * ks][nt], S[2 * ks + 1][nt]);
-      const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(&cur.a[32 * ks + 4 * lg]);
-      const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(&cur.a[32 * ks + 16 + 4 * lg]);
+        for (int nt = 0; nt < F::NTW; ++nt)
+          bS[nt] = *reinterpret_cast<const u32x4_t*>(&sm.Sb[wv0 + 16 * nt + l16][32 * ks + 8 * lg]);
+        Adec[2 * ks] = *reinterpret_cast<const f32x4_t*>(&cur.a[32 * ks + 4 * lg]);
+        Adec[2 * ks + 1] = *reinterpret_cast<const f32x4_t*>(&cur.a[32 * ks + 16 + 4 * lg]);
+      } else {
 #pragma unroll
-      for (int nt = 0; nt < F::NTW; ++nt) {
-        S[2 * ks][nt] *= a0;
-        S[2 * ks + 1][nt] *= a1;
+        for (int nt = 0; nt < F::NTW; ++nt)
+          bS[nt] = acc_pair_to_op(S[2 * ks][nt], S[2 * ks + 1][nt]);
+        const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(&cur.a[32 * ks + 4 * lg]);
+        const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(&cur.a[32 * ks + 16 + 4 * lg]);
+#pragma unroll
+        for (int nt = 0; nt < F::NTW; ++nt) {
+          S[2 * ks][nt] *= a0;
+          S[2 * ks + 1][nt] *= a1;
+        }
       }
 #pragma unroll
       for (int ct = 0; ct < F::CT; ++ct) {
@@ -789,12 +886,28 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
             0, 0);
       }
     }
-    // S^T += Kr^T U^T (the decay was applied in phase A)
+    // S^T += Kr^T U^T (the decay was applied in phase A).  LDS state: each 4-key
+    // piece of the bf16 state is widened, decayed and accumulated in fp32, then
+    // rounded back (one rounding per chunk).
 #pragma unroll
     for (int kt = 0; kt < F::KT; ++kt) {
       const u32x4_t aR = lds_op_tr<F::LDR, F::CT == 2>(&cur.Kr[0][0], 16 * kt, l16, lg);
+      if constexpr (SLDS) {
+        // rows 16 kt + 4 lg + i hold keys key0 + i (the row order of the tiles)
+        const f32x4_t av = Adec[kt];
+        const int key0 = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1);
 #pragma unroll
-      for (int nt = 0; nt < F::NTW; ++nt) S[kt][nt] = mfma_k32(aR, bU[nt], S[kt][nt]);
+        for (int nt = 0; nt < F::NTW; ++nt) {
+          u16* ps = &sm.Sb[wv0 + 16 * nt + l16][key0];
+          const u32x2_t w = *reinterpret_cast<const u32x2_t*>(ps);
+          const f32x4_t t = av * f32x4_t{bflo(w[0]), bfhi(w[0]), bflo(w[1]), bfhi(w[1])};
+          const f32x4_t u = mfma_k32(aR, bU[nt], t);
+          *reinterpret_cast<u32x2_t*>(ps) = u32x2_t{pack_bf16(u[0], u[1]), pack_bf16(u[2], u[3])};
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < F::NTW; ++nt) S[kt][nt] = mfma_k32(aR, bU[nt], S[kt][nt]);
+      }
     }
   };
 
@@ -1290,8 +1403,12 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     // its operands; its matrices and the gate of chunk 1); every wave passes the same
     // barriers.
     if (is_state) {
-      state_in(sbase0);
-      state_cvt();
+      if constexpr (SLDS) {
+        slds_in(sbase0);
+      } else {
+        state_in(sbase0);
+        state_cvt();
+      }
       if (nchunks > 0) {
         lds_barrier();
         lds_barrier();
@@ -1307,7 +1424,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
           lds_barrier();
         }
       }
-      state_out(sbase0);
+      if constexpr (SLDS) slds_out(sbase0);
+      else state_out(sbase0);
     } else if (nchunks > 0) {
       // Raw inputs of chunk c go to register set c % 2, loaded at the start of the
       // phase a whole step before they are used.
@@ -1574,6 +1692,28 @@ hipError_t launch_kda_split(const KdaParams& p, int D, int chunk, int v_tile, hi
   if (D == d && chunk == c && v_tile == vt) return launch_one<d, c, vt, nw, nsw, kModeRecur>(p, stream);
   KDA_SPLIT_SCHEDULES(KDA_SPLIT_LAUNCH)
 #undef KDA_SPLIT_LAUNCH
+  return hipErrorInvalidValue;
+}
+
+// The LDS-state mode's schedules (the state-only schedule at both value tiles).
+#define KDA_SLDS_SCHEDULES(X) \
+  X(128, 32, 128, 12, 4)      \
+  X(128, 32, 64, 12, 4)
+
+bool kda_slds_supported(int D, int chunk, int v_tile) {
+#define KDA_SLDS_SUPPORTED(d, c, vt, nw, nsw) \
+  if (D == d && chunk == c && v_tile == vt) return true;
+  KDA_SLDS_SCHEDULES(KDA_SLDS_SUPPORTED)
+#undef KDA_SLDS_SUPPORTED
+  return false;
+}
+
+hipError_t launch_kda_fwd_slds(const KdaParams& p, int D, int chunk, int v_tile,
+                               hipStream_t stream) {
+#define KDA_SLDS_LAUNCH(d, c, vt, nw, nsw) \
+  if (D == d && chunk == c && v_tile == vt) return launch_one<d, c, vt, nw, nsw, kModeSlds>(p, stream);
+  KDA_SLDS_SCHEDULES(KDA_SLDS_LAUNCH)
+#undef KDA_SLDS_LAUNCH
   return hipErrorInvalidValue;
 }
 

@@ -66,6 +66,12 @@ bool kda_schedule_supported(int D, int chunk, int v_tile);
 // Threads per workgroup of a compiled (D, chunk, v_tile) schedule, 0 if none.
 int kda_schedule_threads(int D, int chunk, int v_tile);
 
+// The LDS-state mode (bf16 state in LDS, fp32 update, one rounding per chunk):
+// whether a schedule has a compiled kernel, and its launch.
+bool kda_slds_supported(int D, int chunk, int v_tile);
+hipError_t launch_kda_fwd_slds(const KdaParams& p, int D, int chunk, int v_tile,
+                               hipStream_t stream);
+
 // Threads per workgroup of the split's prep kernel.
 constexpr int kSplitPrepThreads = 512;
 

@@ -175,6 +175,29 @@ int kda_fwd_ordered(const void* q, const void* k, const void* v, const void* g,
                     int64_t D, void* stream, const int32_t* seq_order);
 
 /*
+ * kda_fwd_bf16_state -- kda_fwd_sched with the recurrent state held in bf16 in
+ * on-chip memory (LDS) instead of fp32 registers, as the page "How FlashKDA
+ * Stores On-Chip Recurrent State in BF16 for Memory Efficiency" describes (its
+ * sections "The BF16 State Layout in Shared Memory" and "State Updates with FP32
+ * FMA"): each chunk's update widens the stored state to fp32, applies the decay
+ * and adds the chunk's term in fp32, then rounds once back to bf16.  An fp32
+ * initial state is rounded to bf16 on entry; the final state is the stored bf16
+ * state (exact in either output dtype).
+ * Runs D = 128 with 32-token chunks (chunk_size 0 or 32; the lower bound must
+ * allow them, |lb| <= 5.112) at v_tile 0, 64 or 128; other schedules return
+ * KDA_ERR_BAD_SCHEDULE.  States are [num_seqs, H, D(v), D(k)] as for kda_fwd;
+ * everything else, including the exact in-place alias, is exactly as kda_fwd.
+ * The results differ from kda_fwd by the per-chunk rounding of the state; it is
+ * an opt-in mode and never chosen automatically.
+ */
+int kda_fwd_bf16_state(const void* q, const void* k, const void* v, const void* g,
+                       const void* beta, float scale, void* out, const float* A_log,
+                       const float* dt_bias, float lower_bound, const void* initial_state,
+                       int initial_state_dtype, void* final_state, int final_state_dtype,
+                       const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T,
+                       int64_t H, int64_t D, void* stream, int chunk_size, int v_tile);
+
+/*
  * kda_fwd_transposed_state -- kda_fwd with both states in the transposed,
  * key-major layout [num_seqs, H, D(k), D(v)]: element (v, k) of a head's
  * state sits at k * D + v (FlashKDA's alternative state layout, its

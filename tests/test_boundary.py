@@ -345,7 +345,7 @@ def test_noalloc_split_rejects_workspaces_beyond_its_scratch(lib):
     cap = lib.kda_split_noalloc_max_bytes()
     assert cap == 64 << 20
     noalloc = lib.kda_fwd_split_noalloc
-    # 96 heads of 2 x 1024 tokens need 96 * 67 records of 33,280 bytes: too many
+    # 96 heads of 2 x 1024 tokens need 96 * 67 records of 35,840 bytes: too many
     a = _args(B=2, T=1024, H=96)
     assert kda.kda_split_workspace_bytes(2048, 2, 96, 128, -5.0) > cap
     assert noalloc(*a[:-2], None, 0, 0) == kda.KDA_ERR_SCRATCH_TOO_SMALL
@@ -354,3 +354,28 @@ def test_noalloc_split_rejects_workspaces_beyond_its_scratch(lib):
         kda.KDA_ERR_BAD_LOWER_BOUND
     assert noalloc(*_args(D=64)[:-2], None, 0, 0) == kda.KDA_ERR_BAD_SCHEDULE
     assert noalloc(*a[:-2], None, 24, 0) == kda.KDA_ERR_BAD_SCHEDULE
+
+
+def test_bf16_state_mode_schedules(lib):
+    """kda_fwd_bf16_state runs D = 128 with 32-token chunks at value tiles 64 and 128
+    only; every other schedule returns KDA_ERR_BAD_SCHEDULE on the host, after the
+    same argument checks as kda_fwd_sched."""
+    f = lib.kda_fwd_bf16_state
+
+    def call(chunk=0, vt=128, **kw):
+        a = _args(**kw)
+        return f(*a[:-2], None, chunk, vt)
+
+    assert call(D=64, vt=64) == kda.KDA_ERR_BAD_SCHEDULE
+    assert call(D=32, vt=32) == kda.KDA_ERR_BAD_SCHEDULE
+    assert call(chunk=16) == kda.KDA_ERR_BAD_SCHEDULE
+    assert call(chunk=8) == kda.KDA_ERR_BAD_SCHEDULE
+    # |lb| = 8 admits 16-token chunks at most: the automatic choice is 16 (no kernel),
+    # and forcing 32 breaks the decay window
+    assert call(lb=-8.0) == kda.KDA_ERR_BAD_SCHEDULE
+    assert call(lb=-8.0, chunk=32) == kda.KDA_ERR_BAD_LOWER_BOUND
+    assert call(vt=32) == kda.KDA_ERR_BAD_SCHEDULE
+    # the shared checks come first
+    assert call(lb=1.0) == kda.KDA_ERR_BAD_LOWER_BOUND
+    assert call(s_out=9 * GB + 2) == kda.KDA_ERR_BAD_ALIAS
+    assert call(q=None) == kda.KDA_ERR_NULL_ARG
