@@ -234,9 +234,11 @@ struct Chunk {
   int h;
 };
 
-// The centred operands Qc and Kc (key order).  The state-only schedule writes the
-// next chunk's while the state waves read the current chunk's, so they live in each
-// slot there; the other schedules keep one copy beside the slots.
+// The centred operands Qc and Kc (key order), and Ki.  The state-only schedule
+// writes the next chunk's while the state waves read the current chunk's, so they
+// live in each slot there (Ki too, since the state waves form the chunk's matrix
+// tiles in the step that uses them; the LDS-state mode has no room for a second Ki
+// and forms them a step earlier); the other schedules keep one copy beside the slots.
 template <class F, bool kHere>
 struct QcKc {};
 template <class F>
@@ -244,10 +246,16 @@ struct QcKc<F, true> {
   u16 Qc[F::C][F::LDQ];
   u16 Kc[F::C][F::LDQ];
 };
+template <class F, bool kHere>
+struct KiBuf {};
+template <class F>
+struct KiBuf<F, true> {
+  u16 Ki[F::C][F::LDQ];
+};
 
 // Prepared operands of one chunk.
-template <class F>
-struct alignas(16) Slot : QcKc<F, F::SO> {
+template <class F, bool kKi>
+struct alignas(16) Slot : QcKc<F, F::SO>, KiBuf<F, kKi> {
   u16 Kr[F::C][F::LDR];      // columns in state-row order (read transposed)
   u16 SOL[F::C][F::LDC];     // X11 2^-16, X22 2^-16 (X = (I + L)^-1 diagonal blocks) and
                              // -L21 2^16: the solve then yields U 2^-16
@@ -269,10 +277,10 @@ struct alignas(16) StateLds<F, true> {
 };
 
 template <class F, int NSLOT, bool kSlds = false>
-struct alignas(16) Smem : QcKc<F, !F::SO>, StateLds<F, kSlds> {  // (Qc, Kc: the chunk whose state side,
+struct alignas(16) Smem : QcKc<F, !F::SO>, KiBuf<F, !F::SO || kSlds>, StateLds<F, kSlds> {  // (Qc, Kc: the chunk whose state side,
                              // matrices and preparation alternate in them)
-  Slot<F> slot[NSLOT];       // two alternate in the chunk loop; the prep kernel uses one
-  u16 Ki[F::C][F::LDQ];
+  Slot<F, F::SO && !kSlds> slot[NSLOT];  // two alternate in the chunk loop; the prep
+                                         // kernel uses one
   float G[F::C][F::LDG];     // inclusive base-2 decay prefix of the chunk being prepared,
                              // inside its row group of the gate layout
   float Goff[F::RG][F::D];   // ... plus this per row group and key: the prefix of the
@@ -437,14 +445,22 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   constexpr bool SLDS = MODE == kModeSlds;
   static_assert(!SLDS || F::SO, "the LDS state runs the state-only schedule only");
   __shared__ Smem<F, MODE == kModePrep ? 1 : 2, SLDS> sm;
+  // the state waves form a chunk's matrix tiles in the step that uses them, from its
+  // own copy of Ki (not in the LDS-state mode: one step earlier, from the one copy)
+  constexpr bool kTilesLate = F::SO && !SLDS;
+  using SlotT = Slot<F, kTilesLate>;
   // The centred operands of the chunk prepared in slot sl.
-  auto qc_of = [&](Slot<F>& sl) -> u16(*)[F::LDQ] {
+  auto qc_of = [&](SlotT& sl) -> u16(*)[F::LDQ] {
     if constexpr (F::SO) return sl.Qc;
     else return sm.Qc;
   };
-  auto kc_of = [&](Slot<F>& sl) -> u16(*)[F::LDQ] {
+  auto kc_of = [&](SlotT& sl) -> u16(*)[F::LDQ] {
     if constexpr (F::SO) return sl.Kc;
     else return sm.Kc;
+  };
+  auto ki_of = [&](SlotT& sl) -> u16(*)[F::LDQ] {
+    if constexpr (kTilesLate) return sl.Ki;
+    else return sm.Ki;
   };
 
   const int tid = threadIdx.x;
@@ -779,7 +795,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   // A: P'^T = Kc S^T and O0' = S Qc^T (P = 2^Ca P', O0 = 2^Ca O0') with the decay
   // S^T <- diag(a) S^T alongside
   // (state_A), then R^T = diag(beta)(V - P^T) in place in P (state_R).
-  auto state_A = [&](Slot<F>& cur) __attribute__((always_inline)) {
+  auto state_A = [&](SlotT& cur) __attribute__((always_inline)) {
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
     // one 32-row key step at a time: its bf16 copy of S^T is live only there, and
     // once it is taken the decay of those rows proceeds while the products run
@@ -817,7 +833,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       }
     }
   };
-  auto state_R = [&](Slot<F>& cur) __attribute__((always_inline)) {
+  auto state_R = [&](SlotT& cur) __attribute__((always_inline)) {
 #pragma unroll
     for (int ct = 0; ct < F::CT; ++ct) {
       const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(&cur.beta[16 * ct + 4 * lg]);
@@ -838,7 +854,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   // formed; with the solve operands' power-of-two factors both halves come out
   // as U 2^-16, the state's own scale.  The output leaves as bf16 straight from
   // the accumulators, through a descriptor bounded to the chunk's valid rows.
-  auto state_B = [&](Slot<F>& cur, const Chunk& ck) __attribute__((always_inline)) {
+  auto state_B = [&](SlotT& cur, const Chunk& ck) __attribute__((always_inline)) {
     u32x4_t bU[F::NTW];
     {
       const u32x4_t aX11 = lds_op_pad(&cur.SOL[l16][0], lg);
@@ -1022,7 +1038,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     return in_row + ((lg & 1) ? below : 0.f) + (lg >= 2 ? lower : 0.f);
   };
   // A (gate waves): gate and inclusive prefix of the next chunk (column layout).
-  auto gate_rows = [&](Slot<F>& nxt, int nxt_valid, auto full, int b) __attribute__((always_inline)) {
+  auto gate_rows = [&](SlotT& nxt, int nxt_valid, auto full, int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int ps = 0; ps < F::SPASS; ++ps) {
       const int col = g_col0 + 2 * F::CPG * ps;
@@ -1092,18 +1108,18 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   };
   // A (gate waves): gate and inclusive prefix of the next chunk (column layout);
   // a full chunk (the common case) skips the per-row end-of-sequence mask.
-  auto gate = [&](Slot<F>& nxt, int nxt_valid, int b = 0) __attribute__((always_inline)) {
+  auto gate = [&](SlotT& nxt, int nxt_valid, int b = 0) __attribute__((always_inline)) {
     if (nxt_valid == C) gate_rows(nxt, nxt_valid, std::true_type{}, b);
     else gate_rows(nxt, nxt_valid, std::false_type{}, b);
   };
   // A (job waves): value tile and beta of the next chunk.
-  auto stage_vb = [&](Slot<F>& nxt, int nxt_valid, int b = 0) __attribute__((always_inline)) {
+  auto stage_vb = [&](SlotT& nxt, int nxt_valid, int b = 0) __attribute__((always_inline)) {
     store_words<F::EPV>(&nxt.V[v_row][v_col], raw_v[b]);
     if (jtid < C) nxt.beta[jtid] = jtid < nxt_valid ? fast_sigmoid(bf2f((u16)raw_b[b])) : 0.f;
   };
   // B: norms and exponent-scaled operands of the next chunk (keys r_col ..
   // r_col + EPT - 1 of chunk row r_row).
-  auto prep_B = [&](Slot<F>& nxt, int b = 0) __attribute__((always_inline)) {
+  auto prep_B = [&](SlotT& nxt, int b = 0) __attribute__((always_inline)) {
     // The prefix, offset and end factor of every position are read first (LDS reads
     // only, in flight while the norms reduce); then each arithmetic kind runs over all
     // positions, so the positions cover each other's latency; then the stores.
@@ -1157,7 +1173,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
         store_bf16<4>(&nxt.Kr[r_row][row_of_key(r_col + r0 + 4 * j)], &oKr[r0 + 4 * j]);
       store_bf16<RUN>(&qc_of(nxt)[r_row][r_col + r0], &oQc[r0]);
       store_bf16<RUN>(&kc_of(nxt)[r_row][r_col + r0], &oKc[r0]);
-      store_bf16<RUN>(&sm.Ki[r_row][r_col + r0], &oKi[r0]);
+      store_bf16<RUN>(&ki_of(nxt)[r_row][r_col + r0], &oKi[r0]);
     }
   };
   // A: the chunk-local matrices of the current chunk from its centred operands,
@@ -1165,10 +1181,10 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   //   L tiles:   L = strictLower(diag(beta) Kc Ki^T); a diagonal tile is inverted
   //              on the spot (X = (I + L)^-1), the lower-left tile is kept as -L21;
   //   Mqk tiles: lowerTri(Qc Ki^T).
-  auto tile = [&](Slot<F>& cur, bool is_l, int ti, int tj) __attribute__((always_inline)) {
+  auto tile = [&](SlotT& cur, bool is_l, int ti, int tj) __attribute__((always_inline)) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     const u16* arow = is_l ? &kc_of(cur)[16 * ti + l16][0] : &qc_of(cur)[16 * ti + l16][0];
-    const u16* brow = &sm.Ki[16 * tj + l16][0];
+    const u16* brow = &ki_of(cur)[16 * tj + l16][0];
 #pragma unroll
     for (int ks = 0; ks < F::KS; ++ks)
       acc = mfma_k32(lds_op_k(arow, 32 * ks, lg), lds_op_k(brow, 32 * ks, lg), acc);
@@ -1230,7 +1246,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   };
   // Matrix job j of a 32-token chunk: 0 L00, 1 L11 (each with its inversion), 2 L10,
   // 3 Mqk10, 4 Mqk00, 5 Mqk11.
-  auto tile_job = [&](Slot<F>& cur, int j) __attribute__((always_inline)) {
+  auto tile_job = [&](SlotT& cur, int j) __attribute__((always_inline)) {
     switch (j) {
       case 0: tile(cur, true, 0, 0); break;
       case 1: tile(cur, true, 1, 1); break;
@@ -1240,10 +1256,10 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       default: tile(cur, false, 1, 1); break;
     }
   };
-  auto chunk_matrices = [&](Slot<F>& cur) __attribute__((always_inline)) {
+  auto chunk_matrices = [&](SlotT& cur) __attribute__((always_inline)) {
     if constexpr (F::SO) {
       // the state-only schedule: the two inversions on job waves 0 and 1; the other
-      // four tiles run on the state waves after their state update
+      // four tiles run on the state waves (see the state-only schedule below)
       if (jw < 2) tile_job(cur, jw);
     } else if constexpr (F::CT == 2) {
 #pragma unroll
@@ -1269,7 +1285,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   constexpr int kRecUnits = 2 * kQU + kRU + 3 * kCU + kAU;
   static_assert(kRecUnits * 16 == kda_record_bytes(D, C), "record layout");
   constexpr int kRecPerJob = (kRecUnits + F::NJW * 64 - 1) / (F::NJW * 64);
-  auto rec_lds = [&](Slot<F>& sl, int u) -> u32x4_t* {
+  auto rec_lds = [&](SlotT& sl, int u) -> u32x4_t* {
     char* b;
     int o;
     if (u < kQU) { b = reinterpret_cast<char*>(&qc_of(sl)[0][0]); o = u; }
@@ -1308,14 +1324,14 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
             u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, base + 16u * u, 0, 0));
     }
   };
-  auto store_rec = [&](Slot<F>& sl) {
+  auto store_rec = [&](SlotT& sl) {
 #pragma unroll
     for (int i = 0; i < kRecPerJob; ++i) {
       const int u = jtid + F::NJW * 64 * i;
       if (u < kRecUnits) *rec_lds(sl, u) = rec_raw[i];
     }
   };
-  auto record_out = [&](Slot<F>& sl) {
+  auto record_out = [&](SlotT& sl) {
     const __amdgpu_buffer_rsrc_t rw = ws_rsrc();
     const uint32_t base = (uint32_t)(rec0 * (int64_t)(kRecUnits * 16));
     for (int u = tid; u < kRecUnits; u += F::NTHR)
@@ -1326,7 +1342,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     raw_b[0] = __builtin_amdgcn_raw_buffer_load_b16(
         make_rsrc(p.beta + ck.tok * H + ck.h, ck.valid * (int)H * 2), off_b, 0, 0);
   };
-  auto stage_b = [&](Slot<F>& nxt, int nxt_valid) {
+  auto stage_b = [&](SlotT& nxt, int nxt_valid) {
     if (jtid < C) nxt.beta[jtid] = jtid < nxt_valid ? fast_sigmoid(bf2f((u16)raw_b[0])) : 0.f;
   };
 
@@ -1360,7 +1376,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
         lds_barrier();
         lds_barrier();
         for (int s = 0; s < nchunks; ++s) {
-          Slot<F>& cur = sm.slot[s & 1];
+          SlotT& cur = sm.slot[s & 1];
           state_A(cur);
           state_R(cur);
           lds_barrier();
@@ -1379,7 +1395,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       load_rec(c1st);
       lds_barrier();
       for (int s = 0; s < nchunks; ++s) {
-        Slot<F>& nxt = sm.slot[(s + 1) & 1];
+        SlotT& nxt = sm.slot[(s + 1) & 1];
         const bool more = s + 1 < nchunks;  // uniform
         const int nxt2 = s + 2 < nchunks ? s + 2 : nchunks - 1;
         if (more) {
@@ -1395,13 +1411,13 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       }
     }
   } else if constexpr (F::SO) {
-    // State-only schedule.  Step s: the state waves run chunk s (A: P, O0, the decay
-    // and R; B: the solve, the state update and the output, then four of chunk s+1's
-    // matrix tiles).  The job waves work one chunk further ahead: A: norms, operands
-    // and value tile of chunk s+1; B: the two inverted tiles of chunk s+1 and the
-    // gate and prefix of chunk s+2.  Three fill phases come first (gate of chunk 0;
-    // its operands; its matrices and the gate of chunk 1); every wave passes the same
-    // barriers.
+    // State-only schedule.  Step s: the state waves run chunk s (A: four of its matrix
+    // tiles, P, O0, the decay and R; B: the solve, the state update and the output;
+    // the LDS-state mode forms the four tiles of chunk s+1 at the end of B instead).
+    // The job waves work one chunk further ahead: A: norms, operands and value tile
+    // of chunk s+1; B: the two inverted tiles of chunk s+1 and the gate and prefix of
+    // chunk s+2.  Three fill phases come first (gate of chunk 0; its operands; its
+    // matrices and the gate of chunk 1); every wave passes the same barriers.
     if (is_state) {
       if constexpr (SLDS) {
         slds_in(sbase0);
@@ -1415,12 +1431,13 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
         tile_job(sm.slot[0], 2 + wave);
         lds_barrier();
         for (int s = 0; s < nchunks; ++s) {
-          Slot<F>& cur = sm.slot[s & 1];
+          SlotT& cur = sm.slot[s & 1];
+          if (kTilesLate && s > 0) tile_job(cur, 2 + wave);
           state_A(cur);
           state_R(cur);
           lds_barrier();
           state_B(cur, ck(s));
-          if (s + 1 < nchunks) tile_job(sm.slot[(s + 1) & 1], 2 + wave);
+          if (!kTilesLate && s + 1 < nchunks) tile_job(sm.slot[(s + 1) & 1], 2 + wave);
           lds_barrier();
         }
       }
@@ -1448,7 +1465,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       // one step; b = s % 2 is a compile-time constant in the unrolled loop below
       auto job_step = [&](int s, auto par) __attribute__((always_inline)) {
         constexpr int b = decltype(par)::value;
-        Slot<F>& nxt = sm.slot[(s + 1) & 1];
+        SlotT& nxt = sm.slot[(s + 1) & 1];
         const bool more = s + 1 < nchunks;   // uniform
         const bool more2 = s + 2 < nchunks;  // uniform
         const int n2 = more2 ? s + 2 : nchunks - 1;
@@ -1488,8 +1505,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
         load_qk(ck(c1st));
         lds_barrier();
         for (int s = 0; s < nchunks; ++s) {
-          Slot<F>& cur = sm.slot[s & 1];
-          Slot<F>& nxt = sm.slot[(s + 1) & 1];
+          SlotT& cur = sm.slot[s & 1];
+          SlotT& nxt = sm.slot[(s + 1) & 1];
           const bool more = s + 1 < nchunks;  // uniform
           const int nxt2 = s + 2 < nchunks ? s + 2 : nchunks - 1;
           state_A(cur);
@@ -1518,8 +1535,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       load_qk(ck(c1st));
       lds_barrier();
       for (int s = 0; s < nchunks; ++s) {
-        Slot<F>& cur = sm.slot[s & 1];
-        Slot<F>& nxt = sm.slot[(s + 1) & 1];
+        SlotT& cur = sm.slot[s & 1];
+        SlotT& nxt = sm.slot[(s + 1) & 1];
         const bool more = s + 1 < nchunks;  // uniform
         const int nxt2 = s + 2 < nchunks ? s + 2 : nchunks - 1;
         if (more) {
@@ -1553,8 +1570,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       load_qk(ck(c1st));
       lds_barrier();
       for (int s = 0; s < nchunks; ++s) {
-        Slot<F>& cur = sm.slot[s & 1];
-        Slot<F>& nxt = sm.slot[(s + 1) & 1];
+        SlotT& cur = sm.slot[s & 1];
+        SlotT& nxt = sm.slot[(s + 1) & 1];
         const bool more = s + 1 < nchunks;  // uniform
         const int nxt2 = s + 2 < nchunks ? s + 2 : nchunks - 1;
         if (is_state) state_A(cur);
