@@ -160,9 +160,10 @@ def main():
     ap.add_argument("--workload", default="batched")
     ap.add_argument("--chunk", type=int, default=None, help="force the chunk size")
     ap.add_argument("--v-tile", type=int, default=0, help="force the value tile")
-    ap.add_argument("--path", choices=("fused", "split"), default="fused",
+    ap.add_argument("--path", choices=("fused", "split", "lds_state"), default="fused",
                     help="fused: the one-kernel forward (kda_fwd_sched); split: the prep and "
-                         "recurrent kernels with a workspace (kda_fwd_split), both timed")
+                         "recurrent kernels with a workspace (kda_fwd_split), both timed; "
+                         "lds_state: the opt-in bf16 LDS state mode (kda_fwd_bf16_state)")
     ap.add_argument("--longest-first", action="store_true",
                     help="packed workloads: dispatch sequences longest first (kda_fwd_ordered); "
                          "the order is computed once, before the timed launches")
@@ -217,6 +218,11 @@ def main():
         ws_bytes = kda.kda_split_workspace_bytes(B * T, args_c[15], H, D, w.lower_bound, 0)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
         call = lambda: lib.kda_fwd_split(*args_c, ws.data_ptr(), ws_bytes, 0, int(args.v_tile))
+    elif args.path == "lds_state":
+        if order is not None:
+            print("--path lds_state takes the index order", file=sys.stderr)
+            sys.exit(2)
+        call = lambda: lib.kda_fwd_bf16_state(*args_c, int(chunk), int(args.v_tile))
     elif order is not None:
         call = lambda: lib.kda_fwd_ordered(*args_c, order.data_ptr())
     else:

@@ -27,7 +27,8 @@ def _close(x, ref, what):
     x = x.to("cpu", torch.float64).numpy()
     mx = float(np.abs(x - ref).max())
     rel = float(np.linalg.norm(x - ref) / max(np.linalg.norm(ref), 1e-300))
-    print("%s: max-abs %.3e rel-L2 %.3e" % (what, mx, rel), flush=True)
+    print("%s: max-abs %.3e rel-L2 %.3e (%.0f%% and %.0f%% of the bounds)"
+          % (what, mx, rel, 100 * mx / MAX_ABS, 100 * rel / REL_L2), flush=True)
     assert mx <= MAX_ABS and rel <= REL_L2, "%s: max-abs %.3e rel-L2 %.3e" % (what, mx, rel)
 
 

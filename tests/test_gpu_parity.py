@@ -34,7 +34,8 @@ def _errors(x, ref):
 
 def _assert_close(x, ref, what):
     mx, rel = _errors(x, ref)
-    print("%s: max-abs %.3e rel-L2 %.3e" % (what, mx, rel), flush=True)
+    print("%s: max-abs %.3e rel-L2 %.3e (%.0f%% and %.0f%% of the bounds)"
+          % (what, mx, rel, 100 * mx / MAX_ABS, 100 * rel / REL_L2), flush=True)
     assert mx <= MAX_ABS and rel <= REL_L2, "%s: max-abs %.3e rel-L2 %.3e" % (what, mx, rel)
 
 
