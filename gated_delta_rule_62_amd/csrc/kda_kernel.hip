@@ -792,11 +792,21 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
 
   // ======================= state side (state waves) ==========================
   f32x4_t P[F::CT][F::NTW], O[F::CT][F::NTW];
+  // the value-tile columns of R, read at the start of phase A (state-only schedule)
+  u32x2_t Vpre[F::CT][F::NTW];
   // A: P'^T = Kc S^T and O0' = S Qc^T (P = 2^Ca P', O0 = 2^Ca O0') with the decay
   // S^T <- diag(a) S^T alongside
   // (state_A), then R^T = diag(beta)(V - P^T) in place in P (state_R).
   auto state_A = [&](SlotT& cur) __attribute__((always_inline)) {
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (F::SO) {
+      // R's value columns, read now so that their latency hides under the products
+#pragma unroll
+      for (int ct = 0; ct < F::CT; ++ct)
+#pragma unroll
+        for (int nt = 0; nt < F::NTW; ++nt)
+          Vpre[ct][nt] = lds_col4<F::LDV>(&cur.V[16 * ct][0], wv0 + 16 * nt, l16, lg);
+    }
     // one 32-row key step at a time: its bf16 copy of S^T is live only there, and
     // once it is taken the decay of those rows proceeds while the products run
 #pragma unroll
@@ -840,7 +850,9 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
 #pragma unroll
       for (int nt = 0; nt < F::NTW; ++nt) {
         // lane: value column wv0 + 16 nt + l16, chunk rows 16 ct + 4 lg .. +3
-        const u32x2_t vv = lds_col4<F::LDV>(&cur.V[16 * ct][0], wv0 + 16 * nt, l16, lg);
+        u32x2_t vv;
+        if constexpr (F::SO) vv = Vpre[ct][nt];
+        else vv = lds_col4<F::LDV>(&cur.V[16 * ct][0], wv0 + 16 * nt, l16, lg);
         P[ct][nt][0] = b4[0] * __builtin_fmaf(-c1, P[ct][nt][0], bflo(vv[0]));
         P[ct][nt][1] = b4[1] * __builtin_fmaf(-c1, P[ct][nt][1], bfhi(vv[0]));
         P[ct][nt][2] = b4[2] * __builtin_fmaf(-c1, P[ct][nt][2], bflo(vv[1]));
