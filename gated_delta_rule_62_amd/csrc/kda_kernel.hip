@@ -1202,6 +1202,10 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
       acc = mfma_k32(lds_op_k(arow, 32 * ks, lg), lds_op_k(brow, 32 * ks, lg), acc);
     const int j = 16 * tj + l16;
     if (!is_l) {
+      // no contraction of the product into the remainder below: every kernel that
+      // forms this tile (here and in the state waves' state_tile) then rounds alike,
+      // whatever it knows of the tile's position at compile time
+#pragma clang fp contract(off)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int i = 16 * ti + 4 * lg + ii;
@@ -1255,6 +1259,37 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) cur.SOL[base + gq + 4 * t][base + m] = to_bf16(kStateDown * x[t]);
+  };
+  // The state waves' tile (job 2 + wave: L10, Mqk10, Mqk00, Mqk11) with its operand
+  // rows chosen arithmetically, so that its reads and products share a block with
+  // the state products; only the stores branch.
+  auto state_tile = [&](SlotT& cur) __attribute__((always_inline)) {
+    const bool t_l = wave == 0;
+    const int t_i = wave == 2 ? 0 : 1;
+    const int t_j = wave == 3 ? 1 : 0;
+    const u16* arow = t_l ? &kc_of(cur)[16 * t_i + l16][0] : &qc_of(cur)[16 * t_i + l16][0];
+    const u16* brow = &ki_of(cur)[16 * t_j + l16][0];
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < F::KS; ++ks)
+      acc = mfma_k32(lds_op_k(arow, 32 * ks, lg), lds_op_k(brow, 32 * ks, lg), acc);
+    const int j = 16 * t_j + l16;
+    if (t_l) {
+      const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(&cur.beta[16 + 4 * lg]);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        cur.SOL[16 + 4 * lg + ii][j] = to_bf16(-kStateUp * b4[ii] * acc[ii]);
+    } else {
+#pragma clang fp contract(off)  // as in tile()
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = 16 * t_i + 4 * lg + ii;
+        const float m = (j <= i) ? acc[ii] * c1i : 0.f;
+        const u16 hi = to_bf16(m);
+        cur.Mqk[i][j] = hi;
+        cur.MqkLo[i][j] = to_bf16(m - bf2f(hi));
+      }
+    }
   };
   // Matrix job j of a 32-token chunk: 0 L00, 1 L11 (each with its inversion), 2 L10,
   // 3 Mqk10, 4 Mqk00, 5 Mqk11.
@@ -1444,7 +1479,7 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
         lds_barrier();
         for (int s = 0; s < nchunks; ++s) {
           SlotT& cur = sm.slot[s & 1];
-          if (kTilesLate && s > 0) tile_job(cur, 2 + wave);
+          if (kTilesLate && s > 0) state_tile(cur);
           state_A(cur);
           state_R(cur);
           lds_barrier();
