@@ -180,10 +180,11 @@ struct Cfg {
   static constexpr bool SO = NW - NSW >= 8;
   static constexpr int JOB_BASE = SPLIT ? NSW : 0;
   static constexpr int NJW = NW - JOB_BASE;      // job waves (they also stage v and beta)
-  // gate waves: the state waves in the role split; the last four job waves in the
-  // state-only schedule (the first four take the two inversions and two other tiles)
+  // gate waves: the state waves in the role split; the first four job waves in the
+  // state-only schedule (the oldest, whom the issue arbiter serves first: the gate
+  // is the job side's longest chain); job waves 4 and 5 take the two inversions
   static constexpr int NGW = SO ? 4 : (SPLIT ? NSW : NW);
-  static constexpr int GATE_BASE = SO ? NJW - 4 : 0;  // first gate wave among the job waves
+  static constexpr int INV_BASE = 4;             // first inversion wave among the job waves
   static constexpr int NOW = SO ? NJW : NW;      // operand waves
   static constexpr int EPT = C * D / (NOW * 64);  // row layout (q, k; operand waves): positions per thread
   static constexpr int TPR = D / EPT;            // threads per chunk row
@@ -943,8 +944,8 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   // Column layout (g, gate, prefix; gate waves): pass ps covers key columns
   // g_col0 + 2 CPG ps and g_col0 + 2 CPG ps + 1 (lane % CPG picks the pair) and
   // chunk rows g_row0 .. g_row0 + RPG - 1 (lane / CPG picks one of RG row groups).
-  const bool is_gate = F::SO ? (is_job && jw >= F::GATE_BASE) : (!F::SPLIT || is_state);
-  const int gw = F::SO ? (is_gate ? jw - F::GATE_BASE : 0)
+  const bool is_gate = F::SO ? (is_job && jw < F::NGW) : (!F::SPLIT || is_state);
+  const int gw = F::SO ? (is_gate ? jw : 0)
                        : ((F::SPLIT && !is_state) ? 0 : wave);  // index among the gate waves
   const int g_col0 = gw * F::SCOLS + 2 * (lane % F::CPG);
   const int g_rg = lane / F::CPG;
@@ -1305,9 +1306,9 @@ __global__ __launch_bounds__(NW * 64) void kda_fwd_kernel(KdaParams p) {
   };
   auto chunk_matrices = [&](SlotT& cur) __attribute__((always_inline)) {
     if constexpr (F::SO) {
-      // the state-only schedule: the two inversions on job waves 0 and 1; the other
+      // the state-only schedule: the two inversions on job waves 4 and 5; the other
       // four tiles run on the state waves (see the state-only schedule below)
-      if (jw < 2) tile_job(cur, jw);
+      if (jw >= F::INV_BASE && jw < F::INV_BASE + 2) tile_job(cur, jw - F::INV_BASE);
     } else if constexpr (F::CT == 2) {
 #pragma unroll
       for (int j = 0; j < 6; ++j) {
