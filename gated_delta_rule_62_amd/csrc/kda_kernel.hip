@@ -53,19 +53,27 @@
 // at -236, a factor below 1e-71, which changes no result representable in fp32.
 //
 // Schedule.  Steps 1-5 only touch chunk-local data, step 6 is the strictly
-// ordered recurrence (section 3's scheduling property).  Waves 0..NSW-1 hold the
-// state; the others (job waves) run the chunk-local matrix jobs.  Step s of the
-// main loop has two phases separated by workgroup barriers that fence LDS only,
-// so the raw inputs of chunk s+2, loaded into registers during step s, stay in
-// flight:
-//   A  P^T, O0 and the decay of S, then gate and prefix of s+1 (in registers),
-//      then R^T for chunk s (state waves)
-//      | L, Mqk and the diagonal inverse blocks of chunk s, value tile of s+1
-//        (job waves)
-//   B  blocked solve, state update and output of chunk s, stored from registers
-//      (state waves) | norms and exponent-scaled operands of s+1 (every wave)
-// Two LDS slots hold the prepared operands of chunks s and s+1 (the page's
-// prep ring, two deep here).
+// ordered recurrence (section 3's scheduling property).  The state waves hold the
+// state; the others (job waves) run chunk-local work.  Step s of the main loop has
+// two phases separated by workgroup barriers that fence LDS only, so raw inputs
+// loaded into registers a step ahead stay in flight.  Two LDS slots hold the
+// prepared operands of chunks s and s+1 (the page's prep ring, two deep here).
+// Two schedules:
+//   state-only (twelve waves: four state waves, eight job waves; value tile D):
+//   A  four matrix tiles of chunk s, P^T, O0 and the decay of S, R^T (state waves)
+//      | q, k, v loads of s+2; norms, operands and value tile of s+1 (job waves)
+//   B  blocked solve, output and state update of chunk s (state waves)
+//      | the two inverted diagonal tiles of s+1 (job waves 4, 5); g loads of s+3,
+//        gate and prefix of s+2 (job waves 0-3)
+//   role split (eight waves: four state waves, four job waves):
+//   A  P^T, O0 and the decay of S, then gate and prefix of s+1, then R^T (state
+//      waves) | L, Mqk and the diagonal inverse blocks of chunk s, value tile of
+//      s+1 (job waves)
+//   B  blocked solve, state update and output of chunk s (state waves) | norms
+//      and exponent-scaled operands of s+1 (every wave)
+// An opt-in mode keeps the state in LDS as bf16 instead (FlashKDA's storage, the
+// page on its bf16 state): the state-only schedule with the state widened, decayed,
+// updated in fp32 and rounded back once per chunk.
 //
 // Layout of the state in registers.  Each wave holds S^T (K rows x its value
 // columns) as 16x16 fp32 accumulator tiles: lane l owns value column (l & 15)
