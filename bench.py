@@ -37,10 +37,15 @@ KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_62_amd", "csrc", f)
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel's code: the sources with // comments, trailing blanks and
+    empty lines removed, so that a comment edit does not orphan the counters."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
