@@ -78,16 +78,32 @@ def test_workload_full(name):
     _check_against_oracle(inp, chunk=w.chunk_size, tag=name)
 
 
-def test_workload_long_sampled_heads():
-    # T = 32768, H = 96: the whole launch runs on the GPU; the oracle recomputes a
-    # sample of heads (each a full 32768-token recurrence) for comparison.
+def test_workload_long_all_heads():
+    # T = 32768, H = 96: the whole launch runs on the GPU; the oracle recomputes every
+    # head (each a full 32768-token recurrence), sixteen heads at a time to bound the
+    # host memory, and the errors are accumulated over all heads.
     w = WORKLOADS["long"]
     inp = make_inputs(w, device=DEV)
     _run(inp)
-    heads = [0, 41, 95]
-    out_ref, fin_ref = _oracle(inp, heads=heads)
-    _assert_close(inp["out"][:, :, heads], out_ref, "long out (heads %s)" % heads)
-    _assert_close(inp["final_state"][:, heads], fin_ref, "long final_state (heads %s)" % heads)
+    H = inp["q"].shape[2]
+    acc = {"out": [0.0, 0.0, 0.0], "final_state": [0.0, 0.0, 0.0]}  # max-abs, |d|^2, |ref|^2
+    for h0 in range(0, H, 16):
+        heads = list(range(h0, min(H, h0 + 16)))
+        print("long: heads %d..%d" % (heads[0], heads[-1]), flush=True)
+        out_ref, fin_ref = _oracle(inp, heads=heads)
+        for what, x, ref in (("out", inp["out"][:, :, heads], out_ref),
+                             ("final_state", inp["final_state"][:, heads], fin_ref)):
+            x = x.detach().to("cpu", torch.float64).numpy()
+            d = x - ref
+            a = acc[what]
+            a[0] = max(a[0], float(np.abs(d).max()))
+            a[1] += float((d * d).sum())
+            a[2] += float((ref * ref).sum())
+    for what, (mx, dd, rr) in acc.items():
+        rel = math.sqrt(dd / rr)
+        print("long %s (all heads): max-abs %.3e rel-L2 %.3e (%.0f%% and %.0f%% of the bounds)"
+              % (what, mx, rel, 100 * mx / MAX_ABS, 100 * rel / REL_L2), flush=True)
+        assert mx <= MAX_ABS and rel <= REL_L2, (what, mx, rel)
 
 
 # --------------------------------------------------------------------------
