@@ -168,31 +168,18 @@ def test_max_head_count_at_the_offset_limit():
 
 def test_half_a_million_short_sequences():
     """2^19 packed sequences of 0-3 tokens (sequence indices, cu_seqlens reads and state
-    offsets at scale).  The oracle recomputes a sample of 64 sequences one by one (the
-    first, a middle and the last ones among them); the sampled outputs and final states
-    are compared as one tensor each."""
+    offsets at scale).  The oracle recomputes the whole packed batch; outputs and final
+    states are compared as one tensor each (a single 3-token, 32-value sequence is too
+    small a tensor for a rel-L2 bound on its own)."""
     n = 1 << 19
     lengths = torch.randint(0, 4, (n,), generator=torch.Generator().manual_seed(25)).tolist()
     w = Workload("many_short", B=1, T=0, H=1, D=32, seed=25, lengths=lengths, state_in="bf16")
     inp = make_inputs(w, device=DEV)
     _run(inp, chunk=16)
-    cu = inp["cu_seqlens"].cpu().tolist()
-    rng = np.random.default_rng(26)
-    sample = sorted(set([0, 1, n // 2, n - 2, n - 1] + rng.integers(0, n, 59).tolist()))
-    got_o, ref_o, got_s, ref_s = [], [], [], []
-    for seq in sample:
-        a, b = cu[seq], cu[seq + 1]
-        cu1 = torch.tensor([0, b - a], dtype=torch.int64)
-        out_ref, fin_ref = oracle.kda_fwd(
-            inp["q"][:, a:b].cpu(), inp["k"][:, a:b].cpu(), inp["v"][:, a:b].cpu(),
-            inp["g"][:, a:b].cpu(), inp["beta"][:, a:b].cpu(), inp["scale"], inp["A_log"].cpu(),
-            inp["dt_bias"].cpu(), inp["lower_bound"], inp["initial_state"][seq:seq + 1].cpu(), cu1)
-        got_o.append(inp["out"][0, a:b].to(torch.float64).cpu().numpy())
-        ref_o.append(out_ref[0])
-        got_s.append(inp["final_state"][seq].to(torch.float64).cpu().numpy())
-        ref_s.append(fin_ref[0])
-    _assert_close(np.concatenate(got_o), np.concatenate(ref_o), "sampled sequences out")
-    _assert_close(np.stack(got_s), np.stack(ref_s), "sampled sequences final_state")
+    print("2^19 sequences: oracle over the whole batch", flush=True)
+    out_ref, fin_ref = _oracle(inp)
+    _assert_close(inp["out"], out_ref, "2^19 sequences out")
+    _assert_close(inp["final_state"], fin_ref, "2^19 sequences final_state")
 
 
 def test_no_initial_state_and_no_final_state():
